@@ -1,0 +1,85 @@
+"""Seeded synthetic workloads for the attention forward pass.
+
+This module only draws inputs: it holds none of the attention arithmetic and
+is the one piece shared by the tests, the benchmark, the oracle checks and the
+GPU path. Every tensor is drawn on the CPU with torch's seeded generator in
+float32 and rounded once to bfloat16 (round-to-nearest-even), so both sides see
+bit-identical inputs.
+
+Workloads (B heads-batch, H heads, N tokens, d head dim), all i.i.d. N(0,1):
+  tiny      1 x  2 x   256 x  64  non-causal
+  causal2k  4 x 16 x  2048 x 128  causal
+  headline  2 x 32 x  8192 x 128  non-causal (the compute-bound shape)
+  long32k   1 x 32 x 32768 x 128  causal
+  drift8k   2 x 16 x  8192 x  64  causal, with a per-key logit drift: key j
+            gets 0.002*j*u and every query gets u, u = ones(d)/sqrt(d), so the
+            running row maximum keeps rising along the keys.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    drift: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        """The float32 softmax scale 1/sqrt(d) handed to both sides."""
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32).item())
+
+    @property
+    def flops(self) -> float:
+        """Attention flop count 4*B*H*N^2*d, halved for causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2.0 if self.causal else f
+
+
+WORKLOADS = [
+    Workload("tiny", 1, 2, 256, 64, False, False, 1001),
+    Workload("causal2k", 4, 16, 2048, 128, True, False, 1002),
+    Workload("headline", 2, 32, 8192, 128, False, False, 1003),
+    Workload("long32k", 1, 32, 32768, 128, True, False, 1004),
+    Workload("drift8k", 2, 16, 8192, 64, True, True, 1005),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def draw(B: int, H: int, N: int, d: int, seed: int, drift: bool = False,
+         drift_rate: float = 0.002):
+    """Draw (q, k, v) as bfloat16 CPU tensors [B,H,N,d], in that order, from one seed."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    if drift:
+        u = torch.full((d,), 1.0 / math.sqrt(d), dtype=torch.float32)
+        j = torch.arange(N, dtype=torch.float32).view(1, 1, N, 1)
+        k += drift_rate * j * u
+        q += u
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def workload_inputs(w: Workload, seed: int | None = None):
+    """Inputs of a named workload (its own seed unless one is given)."""
+    return draw(w.B, w.H, w.N, w.d, w.seed if seed is None else seed, w.drift)
+
+
+def digest(*tensors) -> str:
+    """SHA-256 over the raw bytes of the given tensors (reproducibility record)."""
+    h = hashlib.sha256()
+    for t in tensors:
+        h.update(t.contiguous().view(torch.uint8).numpy().tobytes())
+    return h.hexdigest()

@@ -1,0 +1,13 @@
+"""CPU oracle for exact attention (test infrastructure only).
+
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+may import this package. The product path (the HIP library and its Python
+binding) never imports, links or calls it, and shares no code with it.
+"""
+from .exact import (  # noqa: F401
+    attention,
+    attention_rows,
+    attention_probs,
+    tiled_online_attention,
+    brute_force_attention,
+)

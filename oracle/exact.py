@@ -1,0 +1,207 @@
+"""fp64 CPU oracle for the exact attention forward pass (test infrastructure).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import this
+module. It shares no code with the HIP path and never imports it.
+
+Pages cited (titles as printed, sections as headed on each page):
+  [LK] "FlashAttention 4: faster, more memory-efficient attention for LLMs"
+       (ja.linux-konsole.com)
+  [JG] "Flash Attention" glossary entry (jisaku.com)
+  [SN] "FlashAttention-4: algorithm-kernel fused pipeline for asymmetric
+       hardware scaling" (sns.style)
+
+What is computed ([LK] "Introduction"): queries are multiplied with keys, the
+result is normalised by a softmax and multiplied with the values. The method
+is exact, not an approximation ([JG] "Summary of optimisations", last bullet),
+so the oracle is that definition evaluated in float64:
+
+    s_ij  = scale * sum_k q_ik k_jk                 for j in J(i)
+    m_i   = max_j s_ij,  l_i = sum_j exp(s_ij - m_i)
+    O_i   = sum_j exp(s_ij - m_i) / l_i * v_j
+    LSE_i = m_i + ln(l_i)                           (natural log, scale included)
+
+J(i) = all keys (non-causal) or keys j <= i (causal, lower-triangular mask).
+Inputs are widened exactly to float64 (bfloat16 and float32 values are exact
+in float64), and `scale` is the float32 value the kernel uses, widened.
+
+`tiled_online_attention` is a second, test-only float64 model that follows the
+algorithm the pages describe: tiles of queries and keys, a running maximum and
+running sum per query row ([JG] "Online softmax and recomputation";
+[LK] "Why attention kernels still dominate LLM cost"), and the adaptive policy
+that rescales only when the new maximum exceeds the one in use by more than a
+threshold ([LK] "Smarter online softmax rescaling (new in FA4)"). It works in
+base 2 because the pages name exp2 ([LK] "Software exponential on CUDA cores").
+It pins the algebra of lazy rescaling against `attention`; it is not used to
+produce expected values for the GPU.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+LOG2E = 1.0 / math.log(2.0)
+LN2 = math.log(2.0)
+
+
+def _f64(x) -> np.ndarray:
+    """Widen to float64 (exact for bf16/fp32); accepts numpy arrays or torch CPU tensors."""
+    if hasattr(x, "detach"):  # torch tensor: go through float32, which holds bf16 exactly
+        x = x.detach().to("cpu").float().numpy()
+    a = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(a)):
+        raise ValueError("oracle inputs must be finite")
+    return a
+
+
+def _check_shapes(q, k, v):
+    if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"expected equal [B,H,N,d] shapes, got {q.shape} {k.shape} {v.shape}")
+
+
+def _rows_of_head(qh, kh, vh, rows, causal, scale):
+    """Definition for the query rows `rows` of one head: returns (O[len(rows),d], LSE[len(rows)])."""
+    s = scale * (qh[rows] @ kh.T)                      # [R, N] scores, scale included
+    if causal:
+        keys = np.arange(kh.shape[0])[None, :]
+        s = np.where(keys <= np.asarray(rows)[:, None], s, -np.inf)   # key j visible iff j <= i
+    m = s.max(axis=1, keepdims=True)                   # row maximum (finite: key 0 always visible)
+    e = np.exp(s - m)                                  # exp(-inf) = 0 for masked keys
+    l = e.sum(axis=1, keepdims=True)
+    o = (e @ vh) / l
+    lse = m[:, 0] + np.log(l[:, 0])
+    return o, lse
+
+
+def attention(q, k, v, causal: bool, scale: float, row_block: int = 1024):
+    """Exact attention forward, float64. q, k, v: [B,H,N,d]. Returns (O[B,H,N,d], LSE[B,H,N]).
+
+    Rows are evaluated in blocks of `row_block` only to bound memory; every row's
+    arithmetic is the definition above, independent of the blocking.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    _check_shapes(q, k, v)
+    scale = float(np.float64(scale))
+    B, H, N, d = q.shape
+    o = np.empty((B, H, N, d))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, row_block):
+                rows = np.arange(r0, min(N, r0 + row_block))
+                o[b, h, rows], lse[b, h, rows] = _rows_of_head(q[b, h], k[b, h], v[b, h], rows, causal, scale)
+    return o, lse
+
+
+def attention_rows(q, k, v, causal: bool, scale: float, picks):
+    """Definition evaluated only at sampled outputs.
+
+    picks: iterable of (b, h, rows) with rows a sequence of query indices.
+    Returns a list of (O[len(rows),d], LSE[len(rows)]) in the same order.
+    Used where the full shape would take the CPU too long; each sampled row is
+    computed exactly as in `attention`.
+    """
+    scale = float(np.float64(scale))
+    out = []
+    for b, h, rows in picks:
+        qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
+        rows = np.asarray(rows, dtype=np.int64)
+        out.append(_rows_of_head(qh, kh, vh, rows, causal, scale))
+    return out
+
+
+def attention_probs(q, k, causal: bool, scale: float):
+    """The full softmax matrix P[B,H,N,N] (tiny shapes only), for invariant checks."""
+    q, k = _f64(q), _f64(k)
+    s = scale * np.einsum("bhid,bhjd->bhij", q, k)
+    if causal:
+        n = q.shape[2]
+        s = np.where(np.tril(np.ones((n, n), dtype=bool)), s, -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def brute_force_attention(q, k, v, causal: bool, scale: float):
+    """Pure-Python loops with math.exp over nested lists; tiny inputs only.
+
+    Written without the max shift (plain exp(s)/sum exp(s)), so it also pins
+    that the shifted form used above is the same function.
+    """
+    q, k, v = (_f64(t).tolist() for t in (q, k, v))
+    scale = float(np.float64(scale))
+    B, H, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    o = [[[[0.0] * d for _ in range(N)] for _ in range(H)] for _ in range(B)]
+    lse = [[[0.0] * N for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                keys = range(i + 1) if causal else range(N)
+                w = []
+                for j in keys:
+                    s = 0.0
+                    for c in range(d):
+                        s += q[b][h][i][c] * k[b][h][j][c]
+                    w.append(math.exp(scale * s))
+                z = sum(w)
+                for c in range(d):
+                    o[b][h][i][c] = sum(wj * v[b][h][j][c] for wj, j in zip(w, keys)) / z
+                lse[b][h][i] = math.log(z)
+    return np.array(o), np.array(lse)
+
+
+def tiled_online_attention(q, k, v, causal: bool, scale: float, br: int, bc: int, tau: float):
+    """Test-only float64 model of tiled attention with an online, lazily rescaled softmax.
+
+    Follows the pages' algorithm: each block of `br` query rows streams the keys
+    and values in tiles of `bc`, keeping per row a running maximum and a running
+    sum ([JG] "Online softmax and recomputation"); the exponentials are taken in
+    base 2 ([LK] "Software exponential on CUDA cores"); the stored maximum and
+    the partial results are only rescaled when the tile's maximum exceeds the
+    maximum in use by more than `tau` (log2 units), the adaptive policy of
+    [LK] "Smarter online softmax rescaling (new in FA4)". tau = 0 is the
+    classic policy (rescale on every increase).
+
+    Returns (O, LSE, rescale_events[B,H,N]); the events count the rescales
+    after a row's first tile (which always initialises the row).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    _check_shapes(q, k, v)
+    scale = float(np.float64(scale))
+    B, H, N, d = q.shape
+    o = np.empty((B, H, N, d))
+    lse = np.empty((B, H, N))
+    events = np.zeros((B, H, N), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            for i0 in range(0, N, br):
+                rows = np.arange(i0, min(N, i0 + br))
+                qi = q[b, h, rows]
+                m_used = np.full(len(rows), -np.inf)   # max in use, log2 units
+                l = np.zeros(len(rows))                # running sum of 2^(x - m_used)
+                acc = np.zeros((len(rows), d))         # running sum of 2^(x - m_used) v
+                first = np.ones(len(rows), dtype=bool)
+                for j0 in range(0, N, bc):
+                    keys = np.arange(j0, min(N, j0 + bc))
+                    if causal and keys[0] > rows[-1]:
+                        break                          # tiles above the diagonal hold no visible key
+                    x = (scale * (qi @ k[b, h, keys].T)) * LOG2E   # scaled logits, base 2
+                    if causal:
+                        x = np.where(keys[None, :] <= rows[:, None], x, -np.inf)
+                    m_tile = x.max(axis=1)
+                    grow = m_tile - m_used             # +inf on a row's first visible tile
+                    redo = grow > tau
+                    if np.any(redo):
+                        m_new = np.where(redo, m_tile, m_used)
+                        alpha = np.exp2(m_used - m_new)    # 0 on first tile, 1 where not redone
+                        acc *= alpha[:, None]
+                        l *= alpha
+                        events[b, h, rows] += (redo & ~first).astype(np.int64)
+                        first &= ~(redo & np.isfinite(m_new))
+                        m_used = m_new
+                    p = np.exp2(x - m_used[:, None])   # <= 2^tau where the maximum was not refreshed
+                    l += p.sum(axis=1)
+                    acc += p @ v[b, h, keys]
+                o[b, h, rows] = acc / l[:, None]
+                lse[b, h, rows] = LN2 * (m_used + np.log2(l))
+    return o, lse, events
