@@ -1,0 +1,157 @@
+"""Benchmark of the gfx950 attention forward (one JSON line on stdout).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one attn_fwd call (the whole hot path) on the headline workload:
+B=2, H=32, N=8192, d=128, non-causal, bf16 inputs already resident in device
+memory. The metric is attention TFLOP/s = 4*B*H*N^2*d (halved for causal) /
+kernel time, and its fraction of the MI355X dense bf16 matrix-core peak
+(2500 TFLOP/s). The other workloads are timed too and reported under
+"workloads" for context. The fp64 CPU oracle is timed on the host cores on a
+bounded sample of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-others", action="store_true", help="time only the headline workload")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle time")
+    return ap.parse_args()
+
+
+def time_workload(w, steps, warmup, **kw):
+    """Average kernel time (ms) over `steps` launches, bracketed by device syncs,
+    measured with HIP events on the stream the kernel is launched on."""
+    import torch
+
+    from exact_attention_22_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inputs.workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        binding.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        binding.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, **kw)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return ms
+
+
+def cpu_baseline(w, target_s):
+    """Time the fp64 oracle (as it stands) on a bounded sample: whole heads of the
+    workload, as many as fit the target time; returned in TFLOP/s of the metric."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl absent: report the process's CPU share
+        cores = len(os.sched_getaffinity(0))
+    import oracle
+    from exact_attention_22_amd import inputs
+
+    q, k, v = inputs.draw(1, 1, w.N, w.d, seed=w.seed, drift=w.drift)
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, w.causal, w.scale)
+    one = time.perf_counter() - t0
+    heads = max(1, min(w.B * w.H, int(target_s / max(one, 1e-3))))
+    q, k, v = inputs.draw(1, heads, w.N, w.d, seed=w.seed + 1, drift=w.drift)
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, w.causal, w.scale)
+    dt = time.perf_counter() - t0
+    flops = w.flops / (w.B * w.H) * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads of {w.name} (full rows), {dt:.1f} s fp64 numpy",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by heads with no communication; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from exact_attention_22_amd import binding, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(1)
+    binding.lib()  # fail loudly if the HIP library is missing
+    w = inputs.BY_NAME[args.workload]
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_workload(w, args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+    tflops = w.flops / (ms * 1e-3) / 1e12
+
+    others = {}
+    if not args.no_others:
+        for o in inputs.WORKLOADS:
+            if o.name == w.name:
+                continue
+            oms = time_workload(o, max(5, args.steps // 2), max(3, args.warmup // 2))
+            ot = o.flops / (oms * 1e-3) / 1e12
+            others[o.name] = {"ms": round(oms, 4), "tflops": round(ot, 1),
+                              "frac_peak": round(ot / PEAK_BF16_TFLOPS, 4), "causal": o.causal,
+                              "shape": [o.B, o.H, o.N, o.d]}
+
+    line = {
+        "metric": "attention fwd TFLOP/s (bf16, causal & non-causal) and % of MI355X MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} "
+                               f"bf16 N(0,1) seed {w.seed}",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal},
+        "frac_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "timed_wall_s": round(wall, 2),
+        "workloads": others,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

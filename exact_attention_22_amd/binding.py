@@ -1,0 +1,143 @@
+"""ctypes binding of libattn_fwd.so (argument marshalling only).
+
+Every step of the attention forward runs inside the HIP library. PyTorch only
+provides device memory and the current stream. If the library is missing the
+calls raise; there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
+
+ATTN_OK = 0
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_DIM", 3: "ATTN_ERR_UNSUPPORTED",
+          4: "ATTN_ERR_MISALIGNED", 5: "ATTN_ERR_SCALE", 6: "ATTN_ERR_ALIAS", 7: "ATTN_ERR_HIP",
+          8: "ATTN_ERR_OPTS"}
+O_BF16, O_F32 = 0, 1
+EXPORTS = ["attn_fwd", "attn_fwd_ex", "attn_fwd_check", "attn_fwd_opts_init", "attn_status_str",
+           "attn_last_error", "attn_abi_version", "attn_exp2_poly_host"]
+
+
+class AttnFwdOpts(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_size_t), ("rescale_tau_log2", ctypes.c_float),
+                ("exp2_poly_eighths", ctypes.c_int), ("o_dtype", ctypes.c_int),
+                ("rescale_count", ctypes.c_void_p)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree library once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_attention_22_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        tensor_args = [vp, vp, vp, vp, vp, i, i, i, i, i, f]
+        L.attn_fwd.argtypes = tensor_args + [vp]
+        L.attn_fwd.restype = i
+        L.attn_fwd_ex.argtypes = tensor_args + [ctypes.POINTER(AttnFwdOpts), vp]
+        L.attn_fwd_ex.restype = i
+        L.attn_fwd_check.argtypes = tensor_args + [ctypes.POINTER(AttnFwdOpts)]
+        L.attn_fwd_check.restype = i
+        L.attn_fwd_opts_init.argtypes = [ctypes.POINTER(AttnFwdOpts)]
+        L.attn_fwd_opts_init.restype = None
+        L.attn_status_str.argtypes = [i]
+        L.attn_status_str.restype = ctypes.c_char_p
+        L.attn_last_error.argtypes = []
+        L.attn_last_error.restype = ctypes.c_char_p
+        L.attn_abi_version.argtypes = []
+        L.attn_abi_version.restype = i
+        L.attn_exp2_poly_host.argtypes = [vp, vp, ctypes.c_size_t]
+        L.attn_exp2_poly_host.restype = None
+        _lib = L
+    return _lib
+
+
+def make_opts(tau: float = 8.0, poly_eighths: int = 0, o_dtype: int = O_BF16, rescale_count: int | None = None):
+    opts = AttnFwdOpts()
+    lib().attn_fwd_opts_init(ctypes.byref(opts))
+    opts.rescale_tau_log2 = tau
+    opts.exp2_poly_eighths = poly_eighths
+    opts.o_dtype = o_dtype
+    opts.rescale_count = rescale_count
+    return opts
+
+
+def last_error() -> str:
+    return lib().attn_last_error().decode()
+
+
+def attn_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int, causal: int,
+             scale: float, stream: int | None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return lib().attn_fwd(q, k, v, o, lse, B, H, N, d, int(causal), scale, stream)
+
+
+def attn_fwd_ex(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int, causal: int,
+                scale: float, opts: AttnFwdOpts | None, stream: int | None) -> int:
+    return lib().attn_fwd_ex(q, k, v, o, lse, B, H, N, d, int(causal), scale,
+                             ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def attn_fwd_check(q, k, v, o, lse, B, H, N, d, causal, scale, opts: AttnFwdOpts | None = None) -> int:
+    return lib().attn_fwd_check(q, k, v, o, lse, B, H, N, d, int(causal), scale,
+                                ctypes.byref(opts) if opts is not None else None)
+
+
+def _check_tensor(name, t, shape=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B,H,N,d]")
+    if t.dim() != 4 or (shape is not None and tuple(t.shape) != shape):
+        raise ValueError(f"{name} must have shape {shape or '[B,H,N,d]'}, got {tuple(t.shape)}")
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+              scale: float | None = None, *, tau: float = 8.0, poly_eighths: int = 0,
+              out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+              lse: torch.Tensor | None = None, rescale_count: bool = False):
+    """Exact attention forward on the current stream: returns (O, LSE[, rescale counts]).
+
+    q, k, v: bfloat16 [B,H,N,d] contiguous device tensors; scale defaults to 1/sqrt(d)
+    (as a float32). O has `out_dtype` (bfloat16 or float32); LSE is float32 [B,H,N].
+    """
+    _check_tensor("q", q)
+    shape = tuple(q.shape)
+    _check_tensor("k", k, shape)
+    _check_tensor("v", v, shape)
+    B, H, N, d = shape
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    counts = torch.empty((B, H, N), dtype=torch.int32, device=q.device) if rescale_count else None
+    opts = make_opts(tau, poly_eighths, O_F32 if out_dtype == torch.float32 else O_BF16,
+                     counts.data_ptr() if counts is not None else None)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, H, N, d, causal, scale, opts, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, last_error())
+    return (out, lse, counts) if rescale_count else (out, lse)

@@ -1,0 +1,193 @@
+// attn_fwd.hip - C ABI, argument checks and launch of the gfx950 attention forward kernel.
+//
+// The operation is exact scaled-dot-product attention (page "FlashAttention 4:
+// faster, more memory-efficient attention for LLMs", section "Introduction"),
+// computed by the tiled kernel in attn_fwd_kernel.h. The contract of every
+// entry point is documented in include/attn_fwd.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "attn_fwd.h"
+#include "attn_fwd_kernel.h"
+#include "exp2_poly.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+attn_status_t fail(attn_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+attn_status_t fail(attn_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Tile configuration per head dim: (BC keys per tile, NW waves per workgroup).
+constexpr int kWaves = 4;
+constexpr int kRows = 32 * kWaves;  // query rows per workgroup
+template <int D> struct Cfg;
+template <> struct Cfg<128> { static constexpr int BC = 64; };
+template <> struct Cfg<64> { static constexpr int BC = 128; };
+
+template <int D, bool CAUSAL, bool OF32, int POLY8>
+hipError_t launch(const attn::Params& p, hipStream_t stream) {
+  // hipLaunchKernel reports this launch's own error (no sticky state from other calls).
+  const dim3 grid(p.per_xcd * 8), block(64 * kWaves);
+  void* args[] = {const_cast<attn::Params*>(&p)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, kWaves, CAUSAL, OF32, POLY8>),
+                         grid, block, args, 0, stream);
+}
+
+template <int D, bool CAUSAL, bool OF32>
+hipError_t launch_poly(const attn::Params& p, int poly8, hipStream_t s) {
+  switch (poly8) {
+    case 0: return launch<D, CAUSAL, OF32, 0>(p, s);
+    case 4: return launch<D, CAUSAL, OF32, 4>(p, s);
+    default: return launch<D, CAUSAL, OF32, 8>(p, s);
+  }
+}
+
+template <int D>
+hipError_t launch_d(const attn::Params& p, bool causal, bool of32, int poly8, hipStream_t s) {
+  if (causal)
+    return of32 ? launch_poly<D, true, true>(p, poly8, s) : launch_poly<D, true, false>(p, poly8, s);
+  return of32 ? launch_poly<D, false, true>(p, poly8, s) : launch_poly<D, false, false>(p, poly8, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+void attn_fwd_opts_init(attn_fwd_opts* opts) {
+  if (!opts) return;
+  memset(opts, 0, sizeof *opts);
+  opts->struct_size = sizeof *opts;
+  opts->rescale_tau_log2 = 8.0f;
+  opts->exp2_poly_eighths = 0;
+  opts->o_dtype = ATTN_O_BF16;
+  opts->rescale_count = nullptr;
+}
+
+attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, int B, int H, int N, int d, int causal,
+                             float scale, const attn_fwd_opts* opts) {
+  (void)causal;
+  g_last_error[0] = '\0';
+  attn_fwd_opts def;
+  attn_fwd_opts_init(&def);
+  if (opts) {
+    if (opts->struct_size < sizeof(attn_fwd_opts))
+      return fail(ATTN_ERR_OPTS, "opts->struct_size %zu < %zu", opts->struct_size, sizeof(attn_fwd_opts));
+    def = *opts;
+  }
+  if (B < 0 || H < 0 || N < 0) return fail(ATTN_ERR_DIM, "negative size B=%d H=%d N=%d", B, H, N);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  if (!isfinite(scale)) return fail(ATTN_ERR_SCALE, "scale is not finite");
+  if (!(def.rescale_tau_log2 >= 0.f && def.rescale_tau_log2 <= 64.f))
+    return fail(ATTN_ERR_OPTS, "rescale_tau_log2 %g outside [0, 64]", (double)def.rescale_tau_log2);
+  if (def.exp2_poly_eighths != 0 && def.exp2_poly_eighths != 4 && def.exp2_poly_eighths != 8)
+    return fail(ATTN_ERR_UNSUPPORTED, "exp2_poly_eighths %d (supported: 0, 4, 8)", def.exp2_poly_eighths);
+  if (def.o_dtype != ATTN_O_BF16 && def.o_dtype != ATTN_O_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "o_dtype %d", def.o_dtype);
+  if ((int64_t)B * H * N == 0) return ATTN_OK;  // empty: nothing to do
+
+  const int64_t rows = (int64_t)B * H * N;
+  const int64_t tiles = (int64_t)B * H * ((N + kRows - 1) / kRows);
+  if (rows > (int64_t)1 << 40 || tiles + 8 > INT32_MAX)
+    return fail(ATTN_ERR_DIM, "problem too large: B*H*N=%lld", (long long)rows);
+  if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_NULL, "NULL tensor pointer");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
+    return fail(ATTN_ERR_MISALIGNED, "q, k, v and o must be 16-byte aligned");
+  if ((uintptr_t)lse & 3) return fail(ATTN_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  if (def.rescale_count && ((uintptr_t)def.rescale_count & 3))
+    return fail(ATTN_ERR_MISALIGNED, "rescale_count must be 4-byte aligned");
+
+  const size_t in_bytes = (size_t)rows * d * 2;
+  const size_t o_bytes = (size_t)rows * d * (def.o_dtype == ATTN_O_F32 ? 4 : 2);
+  const size_t l_bytes = (size_t)rows * 4;
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins) {
+    if (overlaps(o, o_bytes, in, in_bytes)) return fail(ATTN_ERR_ALIAS, "o overlaps an input");
+    if (overlaps(lse, l_bytes, in, in_bytes)) return fail(ATTN_ERR_ALIAS, "lse overlaps an input");
+    if (def.rescale_count && overlaps(def.rescale_count, l_bytes, in, in_bytes))
+      return fail(ATTN_ERR_ALIAS, "rescale_count overlaps an input");
+  }
+  if (overlaps(o, o_bytes, lse, l_bytes)) return fail(ATTN_ERR_ALIAS, "o overlaps lse");
+  if (def.rescale_count &&
+      (overlaps(def.rescale_count, l_bytes, o, o_bytes) || overlaps(def.rescale_count, l_bytes, lse, l_bytes)))
+    return fail(ATTN_ERR_ALIAS, "rescale_count overlaps an output");
+  return ATTN_OK;
+}
+
+attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                          int N, int d, int causal, float scale, const attn_fwd_opts* opts, void* stream) {
+  const attn_status_t st = attn_fwd_check(q, k, v, o, lse, B, H, N, d, causal, scale, opts);
+  if (st != ATTN_OK) return st;
+  if ((int64_t)B * H * N == 0) return ATTN_OK;
+  attn_fwd_opts o2;
+  attn_fwd_opts_init(&o2);
+  if (opts) o2 = *opts;
+
+  attn::Params p;
+  p.q = (const __bf16*)q;
+  p.k = (const __bf16*)k;
+  p.v = (const __bf16*)v;
+  p.o = o;
+  p.lse = lse;
+  p.rescale_count = o2.rescale_count;
+  p.N = N;
+  p.nq_tiles = (N + kRows - 1) / kRows;
+  p.total_tiles = B * H * p.nq_tiles;
+  p.per_xcd = (p.total_tiles + 7) / 8;
+  p.c = scale * 1.44269504088896341f;  // log2(e), fp32 product
+  p.tau = o2.rescale_tau_log2;
+  p.neg = scale < 0.f;
+
+  const bool of32 = o2.o_dtype == ATTN_O_F32;
+  const hipError_t err = d == 128 ? launch_d<128>(p, causal != 0, of32, o2.exp2_poly_eighths, (hipStream_t)stream)
+                                  : launch_d<64>(p, causal != 0, of32, o2.exp2_poly_eighths, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+  return ATTN_OK;
+}
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                       int d, int causal, float scale, void* stream) {
+  return attn_fwd_ex(q, k, v, o, lse, B, H, N, d, causal, scale, nullptr, stream);
+}
+
+const char* attn_status_str(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer";
+    case ATTN_ERR_DIM: return "bad dimensions";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dim or option";
+    case ATTN_ERR_MISALIGNED: return "misaligned pointer";
+    case ATTN_ERR_SCALE: return "scale not finite";
+    case ATTN_ERR_ALIAS: return "output overlaps another tensor";
+    case ATTN_ERR_HIP: return "HIP launch error";
+    case ATTN_ERR_OPTS: return "bad options";
+  }
+  return "unknown status";
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+void attn_exp2_poly_host(const float* x, float* y, size_t n) {
+  for (size_t i = 0; i < n; ++i) y[i] = attn_exp2_poly(x[i]);
+}
+
+}  // extern "C"

@@ -1,0 +1,354 @@
+// attn_fwd_kernel.h - tiled exact-attention forward kernel for gfx950 (MI355X).
+//
+// One workgroup computes BR = 32*NW query rows of one (batch, head); each of
+// its NW wavefronts owns 32 rows. The keys and values stream through LDS in
+// tiles of BC rows, the queries stay in registers, and per query row the kernel
+// keeps a running maximum and running sum, so the N x N score matrix never
+// leaves the chip (page "Flash Attention" glossary, sections "Tiling with SRAM"
+// and "Online softmax and recomputation"; page "FlashAttention 4: faster, more
+// memory-efficient attention for LLMs", sections "Why attention kernels still
+// dominate LLM cost" and "What's new in FlashAttention 4").
+//
+// Both products run on the bf16 matrix cores, v_mfma_f32_32x32x16_bf16, in a
+// transposed form chosen for the CDNA register layout:
+//   S^T = K . Q^T   (M = 32 keys, N = 32 queries, K = head dim)
+//   O^T += V^T . P^T (M = 32 value features, N = 32 queries, K = keys)
+// In the 32x32 accumulator layout lane l holds column n = l % 32 and rows
+// 8*(r/4) + 4*(l/32) + r%4 of register r. With queries on the columns, every
+// lane owns ONE query row: the row maximum and row sum are in-lane reductions
+// plus one exchange with lane l^32 (v_permlane32_swap), and the rescale of the
+// output accumulator is a per-lane scalar multiply. The probabilities P^T come
+// out of the first product already in the B-operand layout of the second one
+// (lane l: column l%32, eight consecutive k-slots); the eight keys a lane holds
+// for one k-step are {16h + 8*(j/4) + 4*(l/32) + j%4 : j = 0..7}, so V is staged
+// in LDS transposed (value feature major) with the keys of each group of 16
+// relabelled in that order (bits 2 and 3 of the key index swapped). Then one
+// 16-byte LDS read per lane gives the matching A operand.
+//
+// Online softmax with the adaptive rescale of page "FlashAttention 4: faster,
+// more memory-efficient attention for LLMs", section "Smarter online softmax
+// rescaling (new in FA4)": scores are taken in base 2, x = s * c with
+// c = scale * log2(e) in fp32 (the scale is never folded into bf16 Q); the
+// maximum in use m only moves when a tile's maximum exceeds it by more than
+// tau, and then the partial sum and the output accumulator are rescaled by
+// 2^(m_old - m_new). Otherwise P = 2^(x - m) may exceed 1 (by at most 2^tau),
+// which fp32 accumulation and bf16 P hold without loss of range. The final
+// O = acc / l and LSE = ln 2 * (m + log2 l) are written once.
+#ifndef ATTN_FWD_KERNEL_H
+#define ATTN_FWD_KERNEL_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "exp2_poly.h"
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct Params {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  void* o;
+  float* lse;
+  int* rescale_count;  // optional [B][H][N] int32
+  int N;
+  int nq_tiles;        // ceil(N / BR)
+  int total_tiles;     // B * H * nq_tiles
+  int per_xcd;         // ceil(total_tiles / 8): workgroups per XCD slice
+  float c;             // scale * log2(e), fp32
+  float tau;           // rescale threshold, log2 units
+  int neg;             // scale < 0: the row maximum of s*c is c * min(s)
+};
+
+// Position of key kt (within a tile) in the transposed V staging: bits 2 and 3
+// swapped, so that lane half hl reads keys {4hl..4hl+3, 8+4hl..8+4hl+3} of each
+// 16-key group as 8 consecutive elements.
+__device__ __forceinline__ int vpos(int kt) {
+  return (kt & ~12) | ((kt & 4) << 1) | ((kt & 8) >> 1);
+}
+
+// Max of a value with its copy in lane l^32 (the other half of the same query row).
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_min(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One KV tile of the online softmax for the 32 query rows of a wavefront:
+// S^T = K Q^T, mask (boundary tiles only), tile maximum, adaptive rescale,
+// P = 2^(s*c - m) with the row sum, and O^T += V^T P^T.
+template <int D, int BC, bool CAUSAL, int POLY8, bool MASKED>
+__device__ __forceinline__ void tile_step(const __bf16* __restrict__ ks, const __bf16* __restrict__ vts,
+                                          const bf16x8 (&qreg)[D / 16], f32x16 (&oacc)[D / 32], float& m_used,
+                                          float& l_sum, int& n_rescale, int j0, int N, int my_q, int l32, int hl,
+                                          float c, float tau, bool neg) {
+  constexpr int NC = BC / 32;
+  constexpr int KK = D / 16;
+  constexpr int MT = D / 32;
+  constexpr int KSTR = D + 8;
+  constexpr int VSTR = BC + 8;
+  const float mask_val = neg ? INFINITY : -INFINITY;
+
+  // ---- S^T = K_t Q^T on the matrix cores
+  f32x16 s[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    s[cc] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 a = *(const bf16x8*)(ks + (32 * cc + l32) * KSTR + 16 * kk + 8 * hl);
+      s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[cc], 0, 0, 0);
+    }
+  }
+
+  // ---- mask: keys past N, and (causal) keys after the query
+  if (MASKED) {
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 32 * cc + 8 * (r / 4) + 4 * hl + (r % 4);
+        const bool hide = key >= N || (CAUSAL && key > my_q);
+        s[cc][r] = hide ? mask_val : s[cc][r];
+      }
+  }
+
+  // ---- tile row maximum (of s*c): in-lane, then the lane pair
+  float red;
+  if (!neg) {
+    red = s[0][0];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red = fmaxf(red, s[cc][r]);
+    red = pair_max(red);
+  } else {
+    red = s[0][0];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red = fminf(red, s[cc][r]);
+    red = pair_min(red);
+  }
+  const float m_tile = (red == mask_val) ? -INFINITY : red * c;
+
+  // ---- adaptive rescale: only when the maximum grows by more than tau
+  const float m_new = fmaxf(m_used, m_tile);
+  const bool need = (m_new - m_used) > tau;  // +inf on the row's first tile; NaN (false) if both -inf
+  if (__any(need)) {
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.f;
+    n_rescale += (need && m_used != -INFINITY) ? 1 : 0;
+    m_used = need ? m_new : m_used;
+    l_sum *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[mt][r] *= alpha;
+  }
+
+  // ---- P = 2^(s*c - m), row sum in fp32, bf16 pack in the PV operand order
+  const float mc = -m_used;
+  bf16x8 pb[NC][2];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = fmaf(s[cc][r], c, mc);
+      float e;
+      if (POLY8 == 8 || (POLY8 == 4 && (r & 4)))
+        e = attn_exp2_poly(x);
+      else
+        e = __builtin_amdgcn_exp2f(x);
+      if (MASKED) e = (s[cc][r] == mask_val) ? 0.f : e;
+      l_sum += e;
+      pb[cc][r / 8][r % 8] = (__bf16)e;
+    }
+  }
+
+  // ---- O^T += V_t^T P^T on the matrix cores
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a = *(const bf16x8*)(vts + (32 * mt + l32) * VSTR + 32 * cc + 16 * h + 8 * hl);
+        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc][h], oacc[mt], 0, 0, 0);
+      }
+}
+
+template <int D, int BC, int NW, bool CAUSAL, bool OF32, int POLY8>
+__global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
+  constexpr int BR = 32 * NW;      // query rows per workgroup
+  constexpr int NT = NW * 64;      // threads per workgroup
+  constexpr int NC = BC / 32;      // 32-key chunks per KV tile
+  constexpr int KK = D / 16;       // k-steps of S^T = K Q^T
+  constexpr int MT = D / 32;       // 32-row blocks of O^T
+  constexpr int KSTR = D + 8;      // K row stride in LDS (elements)
+  constexpr int VSTR = BC + 8;     // V^T row stride in LDS (elements)
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int NLD = (BC / 4) * CPR / NT;  // 4-row x 16-byte blocks per thread per tile
+  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert((BC / 4) * CPR % NT == 0, "load split");
+  static_assert(POLY8 == 0 || POLY8 == 4 || POLY8 == 8, "poly split");
+
+  __shared__ __attribute__((aligned(16))) __bf16 ks[BC * KSTR];
+  __shared__ __attribute__((aligned(16))) __bf16 vts[D * VSTR];
+
+  // ---- work decomposition: workgroups are dealt round-robin to the 8 XCDs, so
+  // give XCD x the contiguous slice [x*per_xcd, (x+1)*per_xcd) of tiles: the
+  // q-tiles of one head then share that XCD's L2 for their K/V re-reads.
+  const int wg = blockIdx.x;
+  const int logical = (wg & 7) * p.per_xcd + (wg >> 3);
+  if (logical >= p.total_tiles) return;
+  const int bh = logical / p.nq_tiles;
+  int qt = logical - bh * p.nq_tiles;
+  if (CAUSAL) qt = p.nq_tiles - 1 - qt;  // longest rows first
+  const int N = p.N;
+  const int i0 = qt * BR;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const __bf16* qh = p.q + head;
+  const __bf16* kh = p.k + head;
+  const __bf16* vh = p.v + head;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+  const int wq0 = i0 + wave * 32;
+  const int my_q = wq0 + l32;  // the query row this lane owns
+
+  // ---- Q tile -> registers (B operand of S^T = K Q^T): lane holds Q[my_q][16kk + 8hl + 0..7]
+  bf16x8 qreg[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    if (my_q < N)
+      qreg[kk] = *(const bf16x8*)(qh + (size_t)my_q * D + 16 * kk + 8 * hl);
+    else
+      qreg[kk] = bf16x8{};
+  }
+
+  f32x16 oacc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x16{};
+  float m_used = -INFINITY;  // maximum in use, log2 units
+  float l_sum = 0.f;         // this lane's partial row sum (its 16*NC keys per tile)
+  int n_rescale = 0;
+
+  const float c = p.c;
+  const float tau = p.tau;
+  const bool neg = p.neg != 0;
+
+  const int kv_end = CAUSAL ? min(N, i0 + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+  int t_full = N / BC;  // tiles [0, t_full) need no mask
+  if (CAUSAL) t_full = min(t_full, (i0 + 1) / BC);
+
+  // ---- K/V staging through registers: thread loads NLD blocks of 4 rows x 16 B
+  u32x4 kst[NLD][4], vst[NLD][4];
+  auto gload = [&](int t) {
+    const int j0 = t * BC;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int blk = tid + i * NT;
+      const int col = blk % CPR;
+      const int grp = blk / CPR;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = j0 + 4 * grp + r;
+        if (key < N) {
+          kst[i][r] = *(const u32x4*)(kh + (size_t)key * D + 8 * col);
+          vst[i][r] = *(const u32x4*)(vh + (size_t)key * D + 8 * col);
+        } else {
+          kst[i][r] = u32x4{0, 0, 0, 0};
+          vst[i][r] = u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int blk = tid + i * NT;
+      const int col = blk % CPR;
+      const int grp = blk / CPR;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *(u32x4*)(ks + (4 * grp + r) * KSTR + 8 * col) = kst[i][r];
+      // transpose 4 keys x 8 features into 8 rows of 4 consecutive (relabelled) keys
+      const int pos = vpos(4 * grp);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t a = vst[i][0][w], b = vst[i][1][w], cc = vst[i][2][w], d = vst[i][3][w];
+        // feature 2w: low halves; feature 2w+1: high halves
+        const u32x2 lo = {__builtin_amdgcn_perm(b, a, 0x05040100u), __builtin_amdgcn_perm(d, cc, 0x05040100u)};
+        const u32x2 hi = {__builtin_amdgcn_perm(b, a, 0x07060302u), __builtin_amdgcn_perm(d, cc, 0x07060302u)};
+        *(u32x2*)(vts + (8 * col + 2 * w) * VSTR + pos) = lo;
+        *(u32x2*)(vts + (8 * col + 2 * w + 1) * VSTR + pos) = hi;
+      }
+    }
+  };
+
+  if (n_tiles > 0) gload(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    __syncthreads();  // every wave is done reading the previous tile
+    lstore();
+    __syncthreads();
+    if (t + 1 < n_tiles) gload(t + 1);  // next tile's global loads overlap this tile's math
+
+    const int j0 = t * BC;
+    if (CAUSAL && j0 > wq0 + 31) continue;  // whole tile above this wave's diagonal
+    if (t >= t_full)
+      tile_step<D, BC, CAUSAL, POLY8, true>(ks, vts, qreg, oacc, m_used, l_sum, n_rescale, j0, N, my_q, l32, hl, c,
+                                            tau, neg);
+    else
+      tile_step<D, BC, CAUSAL, POLY8, false>(ks, vts, qreg, oacc, m_used, l_sum, n_rescale, j0, N, my_q, l32, hl, c,
+                                             tau, neg);
+  }
+
+  // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l), written once
+  const float l_tot = pair_sum(l_sum);
+  if (my_q < N) {
+    const float inv = 1.f / l_tot;
+    const size_t row = (size_t)bh * N + my_q;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dv = 32 * mt + 8 * g + 4 * hl;
+        if (OF32) {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = oacc[mt][4 * g + e] * inv;
+          *(f32x4*)((float*)p.o + row * D + dv) = w;
+        } else {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[mt][4 * g + e] * inv);
+          *(bf16x4*)((__bf16*)p.o + row * D + dv) = w;
+        }
+      }
+    if (hl == 0) {
+      p.lse[row] = 0.69314718055994531f * (m_used + log2f(l_tot));
+      if (p.rescale_count) p.rescale_count[row] = n_rescale;
+    }
+  }
+}
+
+}  // namespace attn
+
+#endif

@@ -1,0 +1,142 @@
+/*
+ * attn_fwd.h - C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * Operation: exact scaled-dot-product attention. Queries are multiplied with
+ * the keys, the scores are normalised by a softmax and the result multiplies
+ * the values (page "FlashAttention 4: faster, more memory-efficient attention
+ * for LLMs", section "Introduction"). The result equals standard attention up
+ * to floating-point rounding; it is not an approximation (page "Flash
+ * Attention" glossary, section "Summary of optimisations"). It is computed
+ * tile by tile with a running maximum and running sum per query row, so the
+ * N x N score matrix never reaches device memory (same glossary page, sections
+ * "Tiling with SRAM" and "Online softmax and recomputation").
+ *
+ * For every batch b, head h and query row i (0-based), with J(i) the visible
+ * keys (all keys; or keys j <= i when causal):
+ *
+ *     s_ij   = scale * sum_c q[b,h,i,c] * k[b,h,j,c]
+ *     O[b,h,i,:] = sum_{j in J(i)} softmax_j(s_i.) * v[b,h,j,:]
+ *     LSE[b,h,i] = ln( sum_{j in J(i)} exp(s_ij) )          (natural log, fp32)
+ *
+ * Layout: q, k, v and o are dense row-major [B][H][N][d] tensors (d innermost,
+ * no strides, no padding); lse is dense [B][H][N]. All tensor pointers are
+ * DEVICE pointers. Offsets are computed in 64-bit.
+ *
+ * Ownership: the caller allocates and owns every buffer. The library never
+ * allocates, frees or keeps device memory, uses no workspace and keeps no
+ * state between calls; memory use is linear in N (the O(N) property named on
+ * the glossary page, "Summary of optimisations").
+ *
+ * Asynchrony: every call validates its arguments on the host, then enqueues
+ * one kernel on `stream` (a hipStream_t; NULL = the default stream) and
+ * returns without synchronising. On a validation error nothing is launched
+ * and nothing is written. Device faults surface at the caller's next
+ * synchronisation. Calls are reentrant and thread-safe. Results are bitwise
+ * reproducible for identical inputs and options.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL (with B*H*N > 0) */
+  ATTN_ERR_DIM = 2,         /* B, H or N negative, or sizes overflow the supported range */
+  ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, or an unknown option value */
+  ATTN_ERR_MISALIGNED = 4,  /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
+  ATTN_ERR_SCALE = 5,       /* scale is not finite */
+  ATTN_ERR_ALIAS = 6,       /* o or lse overlaps an input, or o overlaps lse */
+  ATTN_ERR_HIP = 7,         /* the kernel launch failed; details in attn_last_error() */
+  ATTN_ERR_OPTS = 8         /* opts->struct_size too small, or tau out of [0, 64] */
+} attn_status_t;
+
+/* Output element type of o. */
+enum { ATTN_O_BF16 = 0, ATTN_O_F32 = 1 };
+
+/*
+ * Options for attn_fwd_ex. Initialise with attn_fwd_opts_init, then set fields.
+ *
+ * rescale_tau_log2: threshold of the adaptive online rescale (page "FlashAttention
+ *   4: faster, more memory-efficient attention for LLMs", section "Smarter online
+ *   softmax rescaling (new in FA4)"): the stored row maximum and the partial
+ *   results are only rescaled when a tile's maximum exceeds the maximum in use by
+ *   more than tau, measured in log2 units of the scaled scores. 0 = classic
+ *   policy (rescale on every increase). Default 8. Range [0, 64]. Any value gives
+ *   the same result up to rounding.
+ * exp2_poly_eighths: how many of every 8 score columns take 2^x from a cubic
+ *   polynomial on the vector ALU instead of the hardware exp2 instruction (page
+ *   "FlashAttention 4: faster, more memory-efficient attention for LLMs", section
+ *   "Software exponential on CUDA cores"). 0..8; supported values are 0, 4 and 8
+ *   (others return ATTN_ERR_UNSUPPORTED). Default 0.
+ * o_dtype: ATTN_O_BF16 (default; fp32 accumulate, round-to-nearest-even on
+ *   store) or ATTN_O_F32.
+ * rescale_count: optional DEVICE pointer to int32 [B][H][N]; when not NULL the
+ *   kernel stores, per query row, the number of rescales after the row's first
+ *   tile (instrumentation; not part of the result). Must not overlap any tensor.
+ */
+typedef struct attn_fwd_opts {
+  size_t struct_size; /* sizeof(attn_fwd_opts) */
+  float rescale_tau_log2;
+  int exp2_poly_eighths;
+  int o_dtype;
+  int* rescale_count;
+} attn_fwd_opts;
+
+/* Fill *opts with the defaults (struct_size set, tau 8, no polynomial, bf16 O). */
+void attn_fwd_opts_init(attn_fwd_opts* opts);
+
+/*
+ * attn_fwd - exact attention forward with default options.
+ *   q, k, v : const bf16 [B][H][N][d], device, 16-byte aligned, read only.
+ *   o       : bf16 [B][H][N][d], device, 16-byte aligned, written.
+ *   lse     : float [B][H][N], device, 4-byte aligned, written (natural-log LSE).
+ *   B, H, N : >= 0; if any is 0 the call returns ATTN_OK and does nothing
+ *             (pointers may then be NULL). B*H*ceil(N/128) must fit in int32.
+ *   d       : 64 or 128.
+ *   causal  : 0 = all keys visible; nonzero = key j visible to query i iff j <= i.
+ *   scale   : any finite float (0 gives uniform weights; negative is allowed).
+ *   stream  : hipStream_t to enqueue on (NULL = default stream).
+ * Returns ATTN_OK or an error code; on error nothing is launched.
+ */
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/* attn_fwd with options (NULL opts = defaults). Same argument contract. */
+attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, int d, int causal, float scale,
+                          const attn_fwd_opts* opts, void* stream);
+
+/* Host-only argument check used by both entry points: returns the status that
+ * attn_fwd_ex would return before launching (never touches the device). */
+attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, int B, int H, int N, int d, int causal,
+                             float scale, const attn_fwd_opts* opts);
+
+/* Static text for a status code. */
+const char* attn_status_str(attn_status_t status);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/* ATTN_ABI_VERSION of the loaded library. */
+int attn_abi_version(void);
+
+/*
+ * Host evaluation of the kernel's polynomial 2^x (the same inline routine the
+ * device code uses), for checking its error bound on the CPU. Writes
+ * y[i] = 2^x[i] for i < n. Inputs below -127 are clamped to -127.
+ */
+void attn_exp2_poly_host(const float* x, float* y, size_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,80 @@
+"""Shared helpers of the GPU parity tests (call the HIP library, compare with the oracle)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from exact_attention_22_amd import binding
+
+TOL_O = 2e-2     # max |O - O_ref|, bf16 inputs, fp32 accumulation
+TOL_LSE = 1e-3   # max |LSE - LSE_ref|
+
+
+def device():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need an MI355X: torch.cuda.is_available() is False")
+    return torch.device("cuda:0")
+
+
+def note(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(q, k, v, causal, scale, **kw):
+    """q, k, v: bf16 CPU tensors. Returns float64 numpy (O, LSE[, counts])."""
+    dev = device()
+    out = binding.attention(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale, **kw)
+    torch.cuda.synchronize()
+    res = [out[0].float().cpu().numpy().astype(np.float64), out[1].cpu().numpy().astype(np.float64)]
+    if len(out) > 2:
+        res.append(out[2].cpu().numpy())
+    return tuple(res)
+
+
+def max_err(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
+
+
+def assert_close(o, lse, o_ref, lse_ref, tol_o=TOL_O, tol_lse=TOL_LSE, what=""):
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), f"{what}: non-finite output"
+    eo, el = max_err(o, o_ref), max_err(lse, lse_ref)
+    note(f"  {what}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= tol_o, f"{what}: max|dO| {eo:.3e} > {tol_o}"
+    assert el <= tol_lse, f"{what}: max|dLSE| {el:.3e} > {tol_lse}"
+
+
+def sample_picks(B, H, N, seed, full_heads=((0, 0),), block=(32, 64, 128)):
+    """Rows to check on large shapes: every row of a few heads, plus, on every head,
+    the tile edges and 64 seeded rows."""
+    rng = np.random.default_rng(seed)
+    edges = {0, 1, N - 1, N - 2}
+    for b in block:
+        for m in (1, 2, N // b - 1, N // b):
+            for off in (-1, 0):
+                r = m * b + off
+                if 0 <= r < N:
+                    edges.add(r)
+    picks = []
+    for b in range(B):
+        for h in range(H):
+            if (b, h) in full_heads:
+                picks.append((b, h, np.arange(N)))
+            else:
+                rows = sorted(edges | set(rng.integers(0, N, 64).tolist()))
+                picks.append((b, h, np.asarray(rows)))
+    return picks
+
+
+def check_sampled(q, k, v, causal, scale, o, lse, picks, what, tol_o=TOL_O, tol_lse=TOL_LSE):
+    refs = oracle.attention_rows(q, k, v, causal, scale, picks)
+    eo = el = 0.0
+    for (b, h, rows), (o_ref, l_ref) in zip(picks, refs):
+        eo = max(eo, max_err(o[b, h, rows], o_ref))
+        el = max(el, max_err(lse[b, h, rows], l_ref))
+    n = sum(len(r) for _, _, r in picks)
+    note(f"  {what}: {n} sampled rows: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= tol_o and el <= tol_lse, (eo, el)

@@ -1,0 +1,132 @@
+"""C ABI on the host (CPU only): the library loads, exports what include/attn_fwd.h
+declares, and its argument checks return the documented codes without launching."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from exact_attention_22_amd import binding as bnd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn_fwd.h")
+
+# fake, aligned, non-overlapping device addresses: the checks never dereference them
+GB = 1 << 30
+Q, K, V, O, L = 1 * GB, 2 * GB, 3 * GB, 4 * GB, 5 * GB
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = bnd.lib()
+    names = declared_functions()
+    assert set(names) == set(bnd.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert lib.attn_abi_version() == 1
+
+
+def check(*args, **kw):
+    return bnd.attn_fwd_check(*args, **kw)
+
+
+def test_valid_arguments_pass():
+    assert check(Q, K, V, O, L, 2, 32, 8192, 128, 0, 0.088) == bnd.ATTN_OK
+    assert check(Q, K, V, O, L, 1, 1, 1, 64, 1, -3.0) == bnd.ATTN_OK
+    assert check(Q, K, V, O, L, 1, 1, 1, 64, 1, 0.0) == bnd.ATTN_OK
+
+
+def test_empty_is_a_no_op():
+    assert check(None, None, None, None, None, 0, 4, 16, 128, 0, 1.0) == bnd.ATTN_OK
+    assert check(None, None, None, None, None, 1, 4, 0, 128, 1, 1.0) == bnd.ATTN_OK
+    # entry point itself: returns OK without touching the (absent) device
+    assert bnd.attn_fwd(None, None, None, None, None, 1, 1, 0, 64, 0, 1.0, None) == bnd.ATTN_OK
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, K, V, O, L, 1, 1, 8, 64, 0, 1.0), bnd.ATTN_OK + 1),
+    ((Q, K, V, O, None, 1, 1, 8, 64, 0, 1.0), 1),
+    ((Q, K, V, O, L, -1, 1, 8, 64, 0, 1.0), 2),
+    ((Q, K, V, O, L, 1, 1, -8, 64, 0, 1.0), 2),
+    ((Q, K, V, O, L, 1 << 20, 1 << 10, 1 << 20, 64, 0, 1.0), 2),
+    ((Q, K, V, O, L, 1, 1, 8, 96, 0, 1.0), 3),
+    ((Q, K, V, O, L, 1, 1, 8, 256, 0, 1.0), 3),
+    ((Q + 8, K, V, O, L, 1, 1, 8, 64, 0, 1.0), 4),
+    ((Q, K, V, O + 2, L, 1, 1, 8, 64, 0, 1.0), 4),
+    ((Q, K, V, O, L + 2, 1, 1, 8, 64, 0, 1.0), 4),
+    ((Q, K, V, O, L, 1, 1, 8, 64, 0, math.inf), 5),
+    ((Q, K, V, O, L, 1, 1, 8, 64, 0, math.nan), 5),
+    ((Q, K, V, Q, L, 1, 1, 8, 64, 0, 1.0), 6),
+    ((Q, K, V, O, V + 64, 1, 1, 8, 64, 0, 1.0), 6),
+    ((Q, K, V, O, O + 512, 1, 1, 8, 64, 0, 1.0), 6),
+])
+def test_error_codes(args, code):
+    assert check(*args) == code
+    assert bnd.last_error() != ""
+    # the entry point reports the same code and launches nothing
+    assert bnd.attn_fwd(*args, None) == code
+
+
+def test_options():
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(tau=0.0)) == bnd.ATTN_OK
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(tau=-1.0)) == 8
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(tau=65.0)) == 8
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(poly_eighths=3)) == 3
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(o_dtype=2)) == 3
+    for p8 in (0, 4, 8):
+        assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(poly_eighths=p8)) == bnd.ATTN_OK
+    small = bnd.make_opts()
+    small.struct_size = 8
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, small) == 8
+    # fp32 O is twice as large: now overlaps lse placed right after a bf16-sized O
+    rows = 1 * 1 * 8
+    assert check(Q, K, V, O, O + rows * 64 * 2, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(o_dtype=1)) == 6
+    assert check(Q, K, V, O, O + rows * 64 * 2, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(o_dtype=0)) == bnd.ATTN_OK
+    # counter buffer: alignment and aliasing
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(rescale_count=L + 2)) == 4
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(rescale_count=L)) == 6
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(rescale_count=6 * GB)) == bnd.ATTN_OK
+
+
+def test_status_strings():
+    lib = bnd.lib()
+    for code in range(9):
+        assert lib.attn_status_str(code).decode() not in ("", "unknown status")
+    assert lib.attn_status_str(99).decode() == "unknown status"
+
+
+def test_exp2_polynomial_error_bound():
+    """The kernel's software 2^x (the same inline routine, compiled for the host):
+    relative error <= 2e-4 against float64 2^x, exact at integers, monotone.
+    The pages give no coefficients, only that the polynomial is cubic and reaches
+    hardware-level precision (page "FlashAttention 4: faster, more memory-efficient
+    attention for LLMs", section "Software exponential on CUDA cores")."""
+    lib = bnd.lib()
+    f = np.arange(0, 1 << 23, dtype=np.int64).astype(np.float64) / (1 << 23)   # every fp32 in [0,1) ulp-grid
+    x = np.concatenate([f.astype(np.float32),
+                        np.linspace(-126.0, 64.0, 2_000_001, dtype=np.float32),
+                        np.arange(-126, 65, dtype=np.float32)])
+    y = np.empty_like(x)
+    lib.attn_exp2_poly_host(x.ctypes.data, y.ctypes.data, x.size)
+    ref = np.exp2(x.astype(np.float64))
+    rel = np.abs(y.astype(np.float64) / ref - 1.0)
+    assert rel.max() <= 2e-4, rel.max()
+    ints = np.arange(-126, 65, dtype=np.float32)
+    yi = np.empty_like(ints)
+    lib.attn_exp2_poly_host(ints.ctypes.data, yi.ctypes.data, ints.size)
+    assert np.array_equal(yi.astype(np.float64), np.exp2(ints.astype(np.float64)))
+    fs = np.sort(x[: 1 << 23])
+    ys = np.empty_like(fs)
+    lib.attn_exp2_poly_host(fs.ctypes.data, ys.ctypes.data, fs.size)
+    assert np.all(np.diff(ys) >= 0)
+    # clamped far below: tiny, non-negative, no NaN
+    lo = np.array([-1e30, -200.0, -np.inf], dtype=np.float32)
+    ylo = np.empty_like(lo)
+    lib.attn_exp2_poly_host(lo.ctypes.data, ylo.ctypes.data, lo.size)
+    assert np.all(ylo >= 0) and np.all(ylo < 1e-37)
