@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-others", action="store_true", help="time only the headline workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle time")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (calibrates profiler byte counters)")
     return ap.parse_args()
 
 
@@ -114,6 +116,13 @@ def main():
     ms = time_workload(w, args.steps, args.warmup)
     wall = time.perf_counter() - t0
     tflops = w.flops / (ms * 1e-3) / 1e12
+
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     others = {}
     if not args.no_others:

@@ -107,6 +107,8 @@ attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const 
   const int64_t tiles = (int64_t)B * H * ((N + kRows - 1) / kRows);
   if (rows > (int64_t)1 << 40 || tiles + 8 > INT32_MAX)
     return fail(ATTN_ERR_DIM, "problem too large: B*H*N=%lld", (long long)rows);
+  // one head's tensor (plus one tile of padding rows) is addressed with 32-bit byte offsets
+  if ((int64_t)(N + 256) * d * 2 > INT32_MAX) return fail(ATTN_ERR_DIM, "N=%d too long for one head", N);
   if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_NULL, "NULL tensor pointer");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
     return fail(ATTN_ERR_MISALIGNED, "q, k, v and o must be 16-byte aligned");

@@ -20,10 +20,13 @@
 // output accumulator is a per-lane scalar multiply. The probabilities P^T come
 // out of the first product already in the B-operand layout of the second one
 // (lane l: column l%32, eight consecutive k-slots); the eight keys a lane holds
-// for one k-step are {16h + 8*(j/4) + 4*(l/32) + j%4 : j = 0..7}, so V is staged
-// in LDS transposed (value feature major) with the keys of each group of 16
-// relabelled in that order (bits 2 and 3 of the key index swapped). Then one
-// 16-byte LDS read per lane gives the matching A operand.
+// for one k-step are {16h + 8*(j/4) + 4*(l/32) + j%4 : j = 0..7}. The matching
+// A operand (value feature l%32, those eight keys) is a column read of the
+// row-major V tile: gfx950's LDS transpose read ds_read_b64_tr_b16 gives it in
+// two instructions. Within each group of 16 lanes, output lane i, element e is
+// the 16-bit word at (address supplied by lane 4e + i/4) + (i%4) words, so lane
+// i supplies the address of key row i/4 and value-feature quad i%4 and receives
+// four consecutive keys of one value feature.
 //
 // Online softmax with the adaptive rescale of page "FlashAttention 4: faster,
 // more memory-efficient attention for LLMs", section "Smarter online softmax
@@ -67,11 +70,23 @@ struct Params {
   int neg;             // scale < 0: the row maximum of s*c is c * min(s)
 };
 
-// Position of key kt (within a tile) in the transposed V staging: bits 2 and 3
-// swapped, so that lane half hl reads keys {4hl..4hl+3, 8+4hl..8+4hl+3} of each
-// 16-key group as 8 consecutive elements.
-__device__ __forceinline__ int vpos(int kt) {
-  return (kt & ~12) | ((kt & 4) << 1) | ((kt & 8) >> 1);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Four consecutive keys (rows row0 + e, e = 0..3) of value feature col0 + (lane % 16)
+// from a row-major LDS tile with a row stride of `stride` elements.
+__device__ __forceinline__ s16x4 lds_col4(const __bf16* tile, int stride, int row0, int col0, int lane) {
+  const int i = lane & 15;
+  const __bf16* p = tile + (row0 + (i >> 2)) * stride + col0 + 4 * (i & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)p);
+}
+
+// Buffer resource over `bytes` bytes at `base`: raw loads at byte offsets >= bytes
+// return zeros, which zero-fills the rows past N with no branch. The third
+// descriptor word selects 32-bit data format (DATA_FORMAT = 4 in bits 15..18),
+// which raw untyped loads require on gfx9-family parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // Max of a value with its copy in lane l^32 (the other half of the same query row).
@@ -92,7 +107,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 // S^T = K Q^T, mask (boundary tiles only), tile maximum, adaptive rescale,
 // P = 2^(s*c - m) with the row sum, and O^T += V^T P^T.
 template <int D, int BC, bool CAUSAL, int POLY8, bool MASKED>
-__device__ __forceinline__ void tile_step(const __bf16* __restrict__ ks, const __bf16* __restrict__ vts,
+__device__ __forceinline__ void tile_step(const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
                                           const bf16x8 (&qreg)[D / 16], f32x16 (&oacc)[D / 32], float& m_used,
                                           float& l_sum, int& n_rescale, int j0, int N, int my_q, int l32, int hl,
                                           float c, float tau, bool neg) {
@@ -100,20 +115,23 @@ __device__ __forceinline__ void tile_step(const __bf16* __restrict__ ks, const _
   constexpr int KK = D / 16;
   constexpr int MT = D / 32;
   constexpr int KSTR = D + 8;
-  constexpr int VSTR = BC + 8;
+  constexpr int VSTR = D + 32;
   const float mask_val = neg ? INFINITY : -INFINITY;
+  const int lane = 32 * hl + l32;
+  const int g = lane >> 4;  // 16-lane group: value features 16*(g%2).., keys +4*(g/2)
 
   // ---- S^T = K_t Q^T on the matrix cores
+  // (k-step outer, chunk inner: the NC accumulation chains interleave)
   f32x16 s[NC];
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc) {
-    s[cc] = f32x16{};
+  for (int cc = 0; cc < NC; ++cc) s[cc] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
       const bf16x8 a = *(const bf16x8*)(ks + (32 * cc + l32) * KSTR + 16 * kk + 8 * hl);
       s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[cc], 0, 0, 0);
     }
-  }
 
   // ---- mask: keys past N, and (causal) keys after the query
   if (MASKED) {
@@ -186,7 +204,11 @@ __device__ __forceinline__ void tile_step(const __bf16* __restrict__ ks, const _
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 a = *(const bf16x8*)(vts + (32 * mt + l32) * VSTR + 32 * cc + 16 * h + 8 * hl);
+        const int row0 = 32 * cc + 16 * h + 4 * (g >> 1);
+        const int col0 = 32 * mt + 16 * (g & 1);
+        const s16x4 lo = lds_col4(vs, VSTR, row0, col0, lane);
+        const s16x4 hi = lds_col4(vs, VSTR, row0 + 8, col0, lane);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc][h], oacc[mt], 0, 0, 0);
       }
 }
@@ -199,7 +221,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
   constexpr int KK = D / 16;       // k-steps of S^T = K Q^T
   constexpr int MT = D / 32;       // 32-row blocks of O^T
   constexpr int KSTR = D + 8;      // K row stride in LDS (elements)
-  constexpr int VSTR = BC + 8;     // V^T row stride in LDS (elements)
+  constexpr int VSTR = D + 32;     // V row stride in LDS (elements): conflict-free transpose reads
   constexpr int CPR = D / 8;       // 16-byte chunks per row
   constexpr int NLD = (BC / 4) * CPR / NT;  // 4-row x 16-byte blocks per thread per tile
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
@@ -207,7 +229,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
   static_assert(POLY8 == 0 || POLY8 == 4 || POLY8 == 8, "poly split");
 
   __shared__ __attribute__((aligned(16))) __bf16 ks[BC * KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 vts[D * VSTR];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[BC * VSTR];
 
   // ---- work decomposition: workgroups are dealt round-robin to the 8 XCDs, so
   // give XCD x the contiguous slice [x*per_xcd, (x+1)*per_xcd) of tiles: the
@@ -235,12 +257,12 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
 
   // ---- Q tile -> registers (B operand of S^T = K Q^T): lane holds Q[my_q][16kk + 8hl + 0..7]
   bf16x8 qreg[KK];
+  {
+    const __amdgpu_buffer_rsrc_t qrsrc = buffer_rsrc(qh, (uint32_t)N * D * 2);
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    if (my_q < N)
-      qreg[kk] = *(const bf16x8*)(qh + (size_t)my_q * D + 16 * kk + 8 * hl);
-    else
-      qreg[kk] = bf16x8{};
+    for (int kk = 0; kk < KK; ++kk)
+      qreg[kk] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (uint32_t)(my_q * D + 16 * kk + 8 * hl) * 2, 0, 0));
   }
 
   f32x16 oacc[MT];
@@ -261,6 +283,9 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
 
   // ---- K/V staging through registers: thread loads NLD blocks of 4 rows x 16 B
   u32x4 kst[NLD][4], vst[NLD][4];
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t krsrc = buffer_rsrc(kh, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrsrc = buffer_rsrc(vh, head_bytes);
   auto gload = [&](int t) {
     const int j0 = t * BC;
 #pragma unroll
@@ -270,14 +295,9 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
       const int grp = blk / CPR;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = j0 + 4 * grp + r;
-        if (key < N) {
-          kst[i][r] = *(const u32x4*)(kh + (size_t)key * D + 8 * col);
-          vst[i][r] = *(const u32x4*)(vh + (size_t)key * D + 8 * col);
-        } else {
-          kst[i][r] = u32x4{0, 0, 0, 0};
-          vst[i][r] = u32x4{0, 0, 0, 0};
-        }
+        const uint32_t off = (uint32_t)((j0 + 4 * grp + r) * D + 8 * col) * 2;  // >= head_bytes past N: zeros
+        kst[i][r] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, off, 0, 0);
+        vst[i][r] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0);
       }
     }
   };
@@ -289,17 +309,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
       const int grp = blk / CPR;
 #pragma unroll
       for (int r = 0; r < 4; ++r) *(u32x4*)(ks + (4 * grp + r) * KSTR + 8 * col) = kst[i][r];
-      // transpose 4 keys x 8 features into 8 rows of 4 consecutive (relabelled) keys
-      const int pos = vpos(4 * grp);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a = vst[i][0][w], b = vst[i][1][w], cc = vst[i][2][w], d = vst[i][3][w];
-        // feature 2w: low halves; feature 2w+1: high halves
-        const u32x2 lo = {__builtin_amdgcn_perm(b, a, 0x05040100u), __builtin_amdgcn_perm(d, cc, 0x05040100u)};
-        const u32x2 hi = {__builtin_amdgcn_perm(b, a, 0x07060302u), __builtin_amdgcn_perm(d, cc, 0x07060302u)};
-        *(u32x2*)(vts + (8 * col + 2 * w) * VSTR + pos) = lo;
-        *(u32x2*)(vts + (8 * col + 2 * w + 1) * VSTR + pos) = hi;
-      }
+      for (int r = 0; r < 4; ++r) *(u32x4*)(vs + (4 * grp + r) * VSTR + 8 * col) = vst[i][r];
     }
   };
 
@@ -313,10 +324,10 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
     const int j0 = t * BC;
     if (CAUSAL && j0 > wq0 + 31) continue;  // whole tile above this wave's diagonal
     if (t >= t_full)
-      tile_step<D, BC, CAUSAL, POLY8, true>(ks, vts, qreg, oacc, m_used, l_sum, n_rescale, j0, N, my_q, l32, hl, c,
+      tile_step<D, BC, CAUSAL, POLY8, true>(ks, vs, qreg, oacc, m_used, l_sum, n_rescale, j0, N, my_q, l32, hl, c,
                                             tau, neg);
     else
-      tile_step<D, BC, CAUSAL, POLY8, false>(ks, vts, qreg, oacc, m_used, l_sum, n_rescale, j0, N, my_q, l32, hl, c,
+      tile_step<D, BC, CAUSAL, POLY8, false>(ks, vs, qreg, oacc, m_used, l_sum, n_rescale, j0, N, my_q, l32, hl, c,
                                              tau, neg);
   }
 

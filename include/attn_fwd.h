@@ -98,7 +98,9 @@ void attn_fwd_opts_init(attn_fwd_opts* opts);
  *   o       : bf16 [B][H][N][d], device, 16-byte aligned, written.
  *   lse     : float [B][H][N], device, 4-byte aligned, written (natural-log LSE).
  *   B, H, N : >= 0; if any is 0 the call returns ATTN_OK and does nothing
- *             (pointers may then be NULL). B*H*ceil(N/128) must fit in int32.
+ *             (pointers may then be NULL). B*H*ceil(N/128) must fit in int32 and
+ *             (N + 256) * d * 2 must be below 2^31 (one head is addressed with
+ *             32-bit byte offsets), else ATTN_ERR_DIM.
  *   d       : 64 or 128.
  *   causal  : 0 = all keys visible; nonzero = key j visible to query i iff j <= i.
  *   scale   : any finite float (0 gives uniform weights; negative is allowed).

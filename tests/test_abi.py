@@ -55,6 +55,7 @@ def test_empty_is_a_no_op():
     ((Q, K, V, O, L, -1, 1, 8, 64, 0, 1.0), 2),
     ((Q, K, V, O, L, 1, 1, -8, 64, 0, 1.0), 2),
     ((Q, K, V, O, L, 1 << 20, 1 << 10, 1 << 20, 64, 0, 1.0), 2),
+    ((Q, K, V, O, L, 1, 1, (1 << 23), 128, 0, 1.0), 2),
     ((Q, K, V, O, L, 1, 1, 8, 96, 0, 1.0), 3),
     ((Q, K, V, O, L, 1, 1, 8, 256, 0, 1.0), 3),
     ((Q + 8, K, V, O, L, 1, 1, 8, 64, 0, 1.0), 4),
