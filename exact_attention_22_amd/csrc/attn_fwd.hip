@@ -42,28 +42,30 @@ template <> struct Cfg<128> { static constexpr int BC = 64; };
 template <> struct Cfg<64> { static constexpr int BC = 128; };
 
 template <int D, bool CAUSAL, bool OF32, int POLY8>
-hipError_t launch(const attn::Params& p, hipStream_t stream) {
+hipError_t launch(const attn::Params& p, bool neg, hipStream_t stream) {
   // hipLaunchKernel reports this launch's own error (no sticky state from other calls).
+  // A negative scale flips the row maximum of s*c into c * min(s): separate instantiation.
   const dim3 grid(p.per_xcd * 8), block(64 * kWaves);
   void* args[] = {const_cast<attn::Params*>(&p)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, kWaves, CAUSAL, OF32, POLY8>),
-                         grid, block, args, 0, stream);
+  const void* fn = neg ? reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, kWaves, CAUSAL, OF32, POLY8, true>)
+                       : reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, kWaves, CAUSAL, OF32, POLY8, false>);
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 template <int D, bool CAUSAL, bool OF32>
-hipError_t launch_poly(const attn::Params& p, int poly8, hipStream_t s) {
+hipError_t launch_poly(const attn::Params& p, int poly8, bool neg, hipStream_t s) {
   switch (poly8) {
-    case 0: return launch<D, CAUSAL, OF32, 0>(p, s);
-    case 4: return launch<D, CAUSAL, OF32, 4>(p, s);
-    default: return launch<D, CAUSAL, OF32, 8>(p, s);
+    case 0: return launch<D, CAUSAL, OF32, 0>(p, neg, s);
+    case 4: return launch<D, CAUSAL, OF32, 4>(p, neg, s);
+    default: return launch<D, CAUSAL, OF32, 8>(p, neg, s);
   }
 }
 
 template <int D>
-hipError_t launch_d(const attn::Params& p, bool causal, bool of32, int poly8, hipStream_t s) {
+hipError_t launch_d(const attn::Params& p, bool causal, bool of32, int poly8, bool neg, hipStream_t s) {
   if (causal)
-    return of32 ? launch_poly<D, true, true>(p, poly8, s) : launch_poly<D, true, false>(p, poly8, s);
-  return of32 ? launch_poly<D, false, true>(p, poly8, s) : launch_poly<D, false, false>(p, poly8, s);
+    return of32 ? launch_poly<D, true, true>(p, poly8, neg, s) : launch_poly<D, true, false>(p, poly8, neg, s);
+  return of32 ? launch_poly<D, false, true>(p, poly8, neg, s) : launch_poly<D, false, false>(p, poly8, neg, s);
 }
 
 }  // namespace
@@ -153,13 +155,19 @@ attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   p.nq_tiles = (N + kRows - 1) / kRows;
   p.total_tiles = B * H * p.nq_tiles;
   p.per_xcd = (p.total_tiles + 7) / 8;
-  p.c = scale * 1.44269504088896341f;  // log2(e), fp32 product
+  // c = scale * log2(e) in fp32. Masked scores are set to -inf (+inf for a negative
+  // scale) and rely on s*c - m = -inf; for scale == 0 that product would be NaN, so
+  // 0 is replaced by 2^-100: |s| <= 2^17 for bf16 inputs with d <= 128, hence
+  // |s*c| < 2^-82 and 2^(s*c - m) rounds to exactly 1.0f, as with c = 0.
+  p.c = scale * 1.44269504088896341f;
+  if (p.c == 0.f) p.c = 0x1p-100f;
   p.tau = o2.rescale_tau_log2;
-  p.neg = scale < 0.f;
 
   const bool of32 = o2.o_dtype == ATTN_O_F32;
-  const hipError_t err = d == 128 ? launch_d<128>(p, causal != 0, of32, o2.exp2_poly_eighths, (hipStream_t)stream)
-                                  : launch_d<64>(p, causal != 0, of32, o2.exp2_poly_eighths, (hipStream_t)stream);
+  const bool neg = scale < 0.f;
+  const hipError_t err =
+      d == 128 ? launch_d<128>(p, causal != 0, of32, o2.exp2_poly_eighths, neg, (hipStream_t)stream)
+               : launch_d<64>(p, causal != 0, of32, o2.exp2_poly_eighths, neg, (hipStream_t)stream);
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
   return ATTN_OK;
 }

@@ -65,9 +65,8 @@ struct Params {
   int nq_tiles;        // ceil(N / BR)
   int total_tiles;     // B * H * nq_tiles
   int per_xcd;         // ceil(total_tiles / 8): workgroups per XCD slice
-  float c;             // scale * log2(e), fp32
+  float c;             // scale * log2(e) in fp32; +-2^-100 stands in for 0 (see the launcher)
   float tau;           // rescale threshold, log2 units
-  int neg;             // scale < 0: the row maximum of s*c is c * min(s)
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -106,17 +105,17 @@ __device__ __forceinline__ float pair_sum(float x) {
 // One KV tile of the online softmax for the 32 query rows of a wavefront:
 // S^T = K Q^T, mask (boundary tiles only), tile maximum, adaptive rescale,
 // P = 2^(s*c - m) with the row sum, and O^T += V^T P^T.
-template <int D, int BC, bool CAUSAL, int POLY8, bool MASKED>
+template <int D, int BC, bool CAUSAL, int POLY8, bool NEG>
 __device__ __forceinline__ void tile_step(const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
                                           const bf16x8 (&qreg)[D / 16], f32x16 (&oacc)[D / 32], float& m_used,
                                           float& l_sum, int& n_rescale, int j0, int N, int my_q, int l32, int hl,
-                                          float c, float tau, bool neg) {
+                                          float c, float tau, bool masked) {
   constexpr int NC = BC / 32;
   constexpr int KK = D / 16;
   constexpr int MT = D / 32;
   constexpr int KSTR = D + 8;
   constexpr int VSTR = D + 32;
-  const float mask_val = neg ? INFINITY : -INFINITY;
+  constexpr float mask_val = NEG ? INFINITY : -INFINITY;
   const int lane = 32 * hl + l32;
   const int g = lane >> 4;  // 16-lane group: value features 16*(g%2).., keys +4*(g/2)
 
@@ -134,7 +133,7 @@ __device__ __forceinline__ void tile_step(const __bf16* __restrict__ ks, const _
     }
 
   // ---- mask: keys past N, and (causal) keys after the query
-  if (MASKED) {
+  if (masked) {  // boundary tiles only: wave-uniform branch
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
@@ -147,7 +146,7 @@ __device__ __forceinline__ void tile_step(const __bf16* __restrict__ ks, const _
 
   // ---- tile row maximum (of s*c): in-lane, then the lane pair
   float red;
-  if (!neg) {
+  if (!NEG) {
     red = s[0][0];
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
@@ -191,7 +190,6 @@ __device__ __forceinline__ void tile_step(const __bf16* __restrict__ ks, const _
         e = attn_exp2_poly(x);
       else
         e = __builtin_amdgcn_exp2f(x);
-      if (MASKED) e = (s[cc][r] == mask_val) ? 0.f : e;
       l_sum += e;
       pb[cc][r / 8][r % 8] = (__bf16)e;
     }
@@ -213,7 +211,7 @@ __device__ __forceinline__ void tile_step(const __bf16* __restrict__ ks, const _
       }
 }
 
-template <int D, int BC, int NW, bool CAUSAL, bool OF32, int POLY8>
+template <int D, int BC, int NW, bool CAUSAL, bool OF32, int POLY8, bool NEG>
 __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
   constexpr int BR = 32 * NW;      // query rows per workgroup
   constexpr int NT = NW * 64;      // threads per workgroup
@@ -274,7 +272,6 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
 
   const float c = p.c;
   const float tau = p.tau;
-  const bool neg = p.neg != 0;
 
   const int kv_end = CAUSAL ? min(N, i0 + BR) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
@@ -323,12 +320,11 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
 
     const int j0 = t * BC;
     if (CAUSAL && j0 > wq0 + 31) continue;  // whole tile above this wave's diagonal
-    if (t >= t_full)
-      tile_step<D, BC, CAUSAL, POLY8, true>(ks, vs, qreg, oacc, m_used, l_sum, n_rescale, j0, N, my_q, l32, hl, c,
-                                            tau, neg);
-    else
-      tile_step<D, BC, CAUSAL, POLY8, false>(ks, vs, qreg, oacc, m_used, l_sum, n_rescale, j0, N, my_q, l32, hl, c,
-                                             tau, neg);
+    // One instantiation of the tile body for every tile: a second (masked) copy
+    // makes the register allocator shuttle the output accumulators between
+    // register sets on every iteration.
+    tile_step<D, BC, CAUSAL, POLY8, NEG>(ks, vs, qreg, oacc, m_used, l_sum, n_rescale, j0, N, my_q, l32, hl, c, tau,
+                                         t >= t_full);
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l), written once
