@@ -21,7 +21,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_DIM", 3: "ATTN_ERR_UNSU
           8: "ATTN_ERR_OPTS"}
 O_BF16, O_F32 = 0, 1
 EXPORTS = ["attn_fwd", "attn_fwd_ex", "attn_fwd_check", "attn_fwd_opts_init", "attn_status_str",
-           "attn_last_error", "attn_abi_version", "attn_exp2_poly_host"]
+           "attn_last_error", "attn_abi_version", "attn_exp2_poly_host", "attn_fwd_tile_shape"]
 
 
 class AttnFwdOpts(ctypes.Structure):
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.attn_abi_version.restype = i
         L.attn_exp2_poly_host.argtypes = [vp, vp, ctypes.c_size_t]
         L.attn_exp2_poly_host.restype = None
+        L.attn_fwd_tile_shape.argtypes = [i, ctypes.POINTER(i), ctypes.POINTER(i)]
+        L.attn_fwd_tile_shape.restype = i
         _lib = L
     return _lib
 
@@ -76,6 +78,15 @@ def make_opts(tau: float = 8.0, poly_eighths: int = 0, o_dtype: int = O_BF16, re
     opts.o_dtype = o_dtype
     opts.rescale_count = rescale_count
     return opts
+
+
+def tile_shape(d: int) -> tuple[int, int]:
+    """(query rows per workgroup, keys per KV tile) of the kernel for head dim d."""
+    rows, keys = ctypes.c_int(), ctypes.c_int()
+    st = lib().attn_fwd_tile_shape(d, ctypes.byref(rows), ctypes.byref(keys))
+    if st != ATTN_OK:
+        raise AttnError(st, last_error())
+    return rows.value, keys.value
 
 
 def last_error() -> str:

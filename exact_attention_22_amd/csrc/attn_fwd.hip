@@ -38,8 +38,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 constexpr int kWaves = 4;
 constexpr int kRows = 32 * kWaves;  // query rows per workgroup
 template <int D> struct Cfg;
-template <> struct Cfg<128> { static constexpr int BC = 64; };
-template <> struct Cfg<64> { static constexpr int BC = 128; };
+template <> struct Cfg<128> { static constexpr int BC = 32; };
+template <> struct Cfg<64> { static constexpr int BC = 32; };
 
 template <int D, bool CAUSAL, bool OF32, int POLY8>
 hipError_t launch(const attn::Params& p, bool neg, hipStream_t stream) {
@@ -193,6 +193,14 @@ const char* attn_status_str(attn_status_t s) {
 }
 
 const char* attn_last_error(void) { return g_last_error; }
+
+attn_status_t attn_fwd_tile_shape(int d, int* query_rows, int* key_cols) {
+  if (!query_rows || !key_cols) return fail(ATTN_ERR_NULL, "NULL output pointer");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  *query_rows = kRows;
+  *key_cols = d == 128 ? Cfg<128>::BC : Cfg<64>::BC;
+  return ATTN_OK;
+}
 
 int attn_abi_version(void) { return ATTN_ABI_VERSION; }
 

@@ -28,6 +28,17 @@
 // i supplies the address of key row i/4 and value-feature quad i%4 and receives
 // four consecutive keys of one value feature.
 //
+// Data movement: K and V tiles go from HBM/L2 straight into LDS with buffer
+// loads that write LDS (each wave instruction fills 1 KiB: lane l's 16 bytes
+// land at base + 16*l), double-buffered, one barrier per tile. Rows are stored
+// unpadded with an XOR swizzle of their 16-byte chunks, chosen so that both the
+// 16-byte K reads and the V transpose reads are free of bank conflicts. Keys
+// past N read as zeros (buffer range check) and are masked.
+//
+// Software pipeline per wavefront: while the softmax of tile t runs on the
+// VALU, the matrix cores compute S for tile t+1; then O += P_t V_t. The loop is
+// unrolled by two so the two score buffers swap roles without register copies.
+//
 // Online softmax with the adaptive rescale of page "FlashAttention 4: faster,
 // more memory-efficient attention for LLMs", section "Smarter online softmax
 // rescaling (new in FA4)": scores are taken in base 2, x = s * c with
@@ -52,7 +63,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct Params {
   const __bf16* q;
@@ -69,17 +81,6 @@ struct Params {
   float tau;           // rescale threshold, log2 units
 };
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Four consecutive keys (rows row0 + e, e = 0..3) of value feature col0 + (lane % 16)
-// from a row-major LDS tile with a row stride of `stride` elements.
-__device__ __forceinline__ s16x4 lds_col4(const __bf16* tile, int stride, int row0, int col0, int lane) {
-  const int i = lane & 15;
-  const __bf16* p = tile + (row0 + (i >> 2)) * stride + col0 + 4 * (i & 3);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) void*)p);
-}
-
 // Buffer resource over `bytes` bytes at `base`: raw loads at byte offsets >= bytes
 // return zeros, which zero-fills the rows past N with no branch. The third
 // descriptor word selects 32-bit data format (DATA_FORMAT = 4 in bits 15..18),
@@ -88,7 +89,74 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Max of a value with its copy in lane l^32 (the other half of the same query row).
+// LDS layout of a K or V tile: BC rows of D bf16 (2*D bytes), no padding; the
+// 16-byte chunk c of row r is stored at chunk position c ^ swizzle(r).
+// K is read 16 bytes per lane with 16 consecutive rows in each 16-lane phase:
+// the swizzle gives those rows 16 distinct bank groups. V is read with the
+// transpose read: each 32-lane phase touches rows r0..r0+3 (r0 % 4 == 0) and
+// four consecutive chunks; the swizzle spreads them over all 64 banks.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? (4 * (r & 3)) : (4 * ((r >> 1) & 1));
+}
+
+// Loads of one BC-row tile of K or V into an LDS tile buffer. Wave w fills the
+// 1 KiB wave-loads w*LPW .. w*LPW+LPW-1; load_offsets gives each lane's byte
+// offset within a tile (fixed for the whole kernel), and the buffer resource is
+// rebased on the tile's first row in scalar registers, so rows past N read as
+// zeros and no per-tile vector arithmetic is needed. (Free functions: a device
+// member function calling these builtins breaks the kernel's host-side stub.)
+template <int D, int BC, int NW>
+struct LoadShape {
+  static constexpr int CH = D / 8;            // 16-byte chunks per row
+  static constexpr int RPL = 64 / CH;         // rows per wave-load
+  static constexpr int LPW = BC / RPL / NW;   // wave-loads per wave
+  static_assert(BC % (RPL * NW) == 0, "load split");
+};
+
+template <int D, int BC, int NW, bool ISK>
+__device__ __forceinline__ void load_offsets(uint32_t* off, int wave, int lane) {
+  using S = LoadShape<D, BC, NW>;
+#pragma unroll
+  for (int i = 0; i < S::LPW; ++i) {
+    const int r = (wave * S::LPW + i) * S::RPL + lane / S::CH;
+    const int c = (lane % S::CH) ^ (ISK ? kswz<D>(r) : vswz<D>(r));
+    off[i] = (uint32_t)(r * D + 8 * c) * 2;
+  }
+}
+
+template <int D, int BC, int NW>
+__device__ __forceinline__ void load_tile(const uint32_t* off, const __bf16* head, int N, int j0, char* buf,
+                                          int wave) {
+  using S = LoadShape<D, BC, NW>;
+  const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(head + (size_t)j0 * D, (uint32_t)(N - j0) * D * 2);
+#pragma unroll
+  for (int i = 0; i < S::LPW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(buf + (wave * S::LPW + i) * 1024), 16, off[i], 0, 0, 0);
+}
+
+// K fragment (A operand of S^T = K Q^T): row R, 16-byte chunk c.
+template <int D>
+__device__ __forceinline__ bf16x8 k_frag(const char* kb, int R, int c) {
+  return *(const bf16x8*)(kb + R * (2 * D) + ((c ^ kswz<D>(R)) << 4));
+}
+
+// Four consecutive keys (rows row0 + e, e = 0..3) of value feature col0 + (lane % 16)
+// from the swizzled V tile, by the LDS transpose read.
+template <int D>
+__device__ __forceinline__ s16x4 v_col4(const char* vb, int row0, int col0, int lane) {
+  const int i = lane & 15;
+  const int r = row0 + (i >> 2);
+  const int dv = col0 + 4 * (i & 3);
+  const char* p = vb + r * (2 * D) + (((dv >> 3) ^ vswz<D>(r)) << 4) + ((dv & 7) << 1);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_void*)p);
+}
+
+// Max / min / sum of a value with its copy in lane l^32 (the other half of the same query row).
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -102,132 +170,134 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One KV tile of the online softmax for the 32 query rows of a wavefront:
-// S^T = K Q^T, mask (boundary tiles only), tile maximum, adaptive rescale,
-// P = 2^(s*c - m) with the row sum, and O^T += V^T P^T.
-template <int D, int BC, bool CAUSAL, int POLY8, bool NEG>
-__device__ __forceinline__ void tile_step(const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
-                                          const bf16x8 (&qreg)[D / 16], f32x16 (&oacc)[D / 32], float& m_used,
-                                          float& l_sum, int& n_rescale, int j0, int N, int my_q, int l32, int hl,
-                                          float c, float tau, bool masked) {
-  constexpr int NC = BC / 32;
+// Part of S^T = K Q^T for the K tile in `kb`: the MFMAs with flat index
+// cc * (D/16) + kk in [F0, F1) (chunk cc of 32 keys, k-step kk); a chunk's chain
+// starts from zero at kk = 0.
+template <int D, int NC, int F0, int F1>
+__device__ __forceinline__ void qk_part(const char* kb, const bf16x8 (&qreg)[D / 16], f32x16 (&s)[NC], int l32,
+                                        int hl) {
   constexpr int KK = D / 16;
+#pragma unroll
+  for (int f = F0; f < F1; ++f) {
+    const int cc = f / KK, kk = f % KK;
+    if (kk == 0) s[cc] = f32x16{};
+    s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(kb, 32 * cc + l32, 2 * kk + hl), qreg[kk], s[cc], 0, 0,
+                                                    0);
+  }
+}
+
+// Running softmax state of the 32 query rows of a wavefront (one row per lane pair).
+template <int D>
+struct RowState {
+  f32x16 oacc[D / 32];  // O^T accumulator (unnormalised)
+  float m_used;          // maximum in use, log2 units
+  float l_sum;           // this lane's partial row sum
+  int n_rescale;
+};
+
+// One KV tile for a wavefront, software-pipelined: the softmax of tile t (scores
+// in s_cur) overlaps the S^T MFMAs of tile t+1 (into s_nxt, K tile in kb_nxt),
+// then O^T += V_t^T P_t^T with V_t in vb_cur.
+template <int D, int BC, bool CAUSAL, int POLY8, bool NEG>
+__device__ __forceinline__ void tile_step(RowState<D>& st, f32x16 (&s_cur)[BC / 32], f32x16 (&s_nxt)[BC / 32],
+                                          const bf16x8 (&qreg)[D / 16], const char* kb_nxt, const char* vb_cur,
+                                          bool masked, int j0, int N, int my_q, int lane, float c, float tau) {
+  constexpr int NC = BC / 32;
   constexpr int MT = D / 32;
-  constexpr int KSTR = D + 8;
-  constexpr int VSTR = D + 32;
   constexpr float mask_val = NEG ? INFINITY : -INFINITY;
-  const int lane = 32 * hl + l32;
-  const int g = lane >> 4;  // 16-lane group: value features 16*(g%2).., keys +4*(g/2)
+  const int l32 = lane & 31, hl = lane >> 5, g = lane >> 4;
 
-  // ---- S^T = K_t Q^T on the matrix cores
-  // (k-step outer, chunk inner: the NC accumulation chains interleave)
-  f32x16 s[NC];
-#pragma unroll
-  for (int cc = 0; cc < NC; ++cc) s[cc] = f32x16{};
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      const bf16x8 a = *(const bf16x8*)(ks + (32 * cc + l32) * KSTR + 16 * kk + 8 * hl);
-      s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[cc], 0, 0, 0);
-    }
+  // First half of the next tile's scores: independent of this tile's softmax.
+  // Computed unconditionally (past the last tile, or past a causal wavefront's
+  // diagonal, the result is unused): straight-line code keeps the two score
+  // buffers in place.
+  qk_part<D, NC, 0, NC * (D / 16) / 2>(kb_nxt, qreg, s_nxt, l32, hl);
 
-  // ---- mask: keys past N, and (causal) keys after the query
-  if (masked) {  // boundary tiles only: wave-uniform branch
+  // ---- mask: keys past N, and (causal) keys after the query; boundary tiles only
+  if (masked) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 32 * cc + 8 * (r / 4) + 4 * hl + (r % 4);
         const bool hide = key >= N || (CAUSAL && key > my_q);
-        s[cc][r] = hide ? mask_val : s[cc][r];
+        s_cur[cc][r] = hide ? mask_val : s_cur[cc][r];
       }
   }
 
-  // ---- tile row maximum (of s*c): in-lane, then the lane pair
-  float red;
-  if (!NEG) {
-    red = s[0][0];
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red = fmaxf(red, s[cc][r]);
-    red = pair_max(red);
-  } else {
-    red = s[0][0];
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red = fminf(red, s[cc][r]);
-    red = pair_min(red);
-  }
-  const float m_tile = (red == mask_val) ? -INFINITY : red * c;
-
-  // ---- adaptive rescale: only when the maximum grows by more than tau
-  const float m_new = fmaxf(m_used, m_tile);
-  const bool need = (m_new - m_used) > tau;  // +inf on the row's first tile; NaN (false) if both -inf
-  if (__any(need)) {
-    const float alpha = need ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.f;
-    n_rescale += (need && m_used != -INFINITY) ? 1 : 0;
-    m_used = need ? m_new : m_used;
-    l_sum *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[mt][r] *= alpha;
-  }
-
-  // ---- P = 2^(s*c - m), row sum in fp32, bf16 pack in the PV operand order
-  const float mc = -m_used;
-  bf16x8 pb[NC][2];
-#pragma unroll
-  for (int cc = 0; cc < NC; ++cc) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float x = fmaf(s[cc][r], c, mc);
-      float e;
-      if (POLY8 == 8 || (POLY8 == 4 && (r & 4)))
-        e = attn_exp2_poly(x);
-      else
-        e = __builtin_amdgcn_exp2f(x);
-      l_sum += e;
-      pb[cc][r / 8][r % 8] = (__bf16)e;
-    }
-  }
-
-  // ---- O^T += V_t^T P^T on the matrix cores
+  // ---- tile row maximum of s*c: in-lane, then the lane pair
+  float red = s_cur[0][0];
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int r = 0; r < 16; ++r) red = NEG ? fminf(red, s_cur[cc][r]) : fmaxf(red, s_cur[cc][r]);
+  red = NEG ? pair_min(red) : pair_max(red);
+  const float m_tile = red * c;  // -inf when every key of the row is masked (c is never 0)
+
+  // ---- adaptive rescale: only when the maximum grows by more than tau
+  const float m_new = fmaxf(st.m_used, m_tile);
+  const bool need = (m_new - st.m_used) > tau;  // +inf on the row's first tile; NaN (false) if both -inf
+  if (__any(need)) {
+    const float alpha = need ? __builtin_amdgcn_exp2f(st.m_used - m_new) : 1.f;
+    st.n_rescale += (need && st.m_used != -INFINITY) ? 1 : 0;
+    st.m_used = need ? m_new : st.m_used;
+    st.l_sum *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[mt][r] *= alpha;
+  }
+
+  // ---- second half of the next tile's scores
+  qk_part<D, NC, NC * (D / 16) / 2, NC * (D / 16)>(kb_nxt, qreg, s_nxt, l32, hl);
+
+  // ---- P = 2^(s*c - m), row sum in fp32, bf16 pack in the PV operand order;
+  //      O^T += V^T P^T per 16-key step as soon as its P fragment is packed
+  const float mc = -st.m_used;
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 pb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 8 * h + j;
+        const float x = fmaf(s_cur[cc][r], c, mc);
+        float e;
+        if (POLY8 == 8 || (POLY8 == 4 && (r & 4)))
+          e = attn_exp2_poly(x);
+        else
+          e = __builtin_amdgcn_exp2f(x);
+        st.l_sum += e;
+        pb[j] = (__bf16)e;
+      }
+      const int row0 = 32 * cc + 16 * h + 4 * (g >> 1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int row0 = 32 * cc + 16 * h + 4 * (g >> 1);
         const int col0 = 32 * mt + 16 * (g & 1);
-        const s16x4 lo = lds_col4(vs, VSTR, row0, col0, lane);
-        const s16x4 hi = lds_col4(vs, VSTR, row0 + 8, col0, lane);
+        const s16x4 lo = v_col4<D>(vb_cur, row0, col0, lane);
+        const s16x4 hi = v_col4<D>(vb_cur, row0 + 8, col0, lane);
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc][h], oacc[mt], 0, 0, 0);
+        st.oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, st.oacc[mt], 0, 0, 0);
       }
+    }
+  }
 }
 
 template <int D, int BC, int NW, bool CAUSAL, bool OF32, int POLY8, bool NEG>
 __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
   constexpr int BR = 32 * NW;      // query rows per workgroup
-  constexpr int NT = NW * 64;      // threads per workgroup
   constexpr int NC = BC / 32;      // 32-key chunks per KV tile
   constexpr int KK = D / 16;       // k-steps of S^T = K Q^T
   constexpr int MT = D / 32;       // 32-row blocks of O^T
-  constexpr int KSTR = D + 8;      // K row stride in LDS (elements)
-  constexpr int VSTR = D + 32;     // V row stride in LDS (elements): conflict-free transpose reads
-  constexpr int CPR = D / 8;       // 16-byte chunks per row
-  constexpr int NLD = (BC / 4) * CPR / NT;  // 4-row x 16-byte blocks per thread per tile
+  constexpr int TILEB = BC * D * 2;
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert((BC / 4) * CPR % NT == 0, "load split");
   static_assert(POLY8 == 0 || POLY8 == 4 || POLY8 == 8, "poly split");
 
-  __shared__ __attribute__((aligned(16))) __bf16 ks[BC * KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 vs[BC * VSTR];
+  // K tile buffers 0,1 then V tile buffers 0,1
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
+  char* const kbuf[2] = {smem, smem + TILEB};
+  char* const vbuf[2] = {smem + 2 * TILEB, smem + 3 * TILEB};
 
   // ---- work decomposition: workgroups are dealt round-robin to the 8 XCDs, so
   // give XCD x the contiguous slice [x*per_xcd, (x+1)*per_xcd) of tiles: the
@@ -241,9 +311,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
   const int N = p.N;
   const int i0 = qt * BR;
   const size_t head = (size_t)bh * (size_t)N * D;
-  const __bf16* qh = p.q + head;
-  const __bf16* kh = p.k + head;
-  const __bf16* vh = p.v + head;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -253,105 +321,93 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
   const int wq0 = i0 + wave * 32;
   const int my_q = wq0 + l32;  // the query row this lane owns
 
-  // ---- Q tile -> registers (B operand of S^T = K Q^T): lane holds Q[my_q][16kk + 8hl + 0..7]
+  const __bf16* const kh = p.k + head;
+  const __bf16* const vh = p.v + head;
+  constexpr int LPW = LoadShape<D, BC, NW>::LPW;
+  uint32_t koff[LPW], voff[LPW];
+  load_offsets<D, BC, NW, true>(koff, wave, lane);
+  load_offsets<D, BC, NW, false>(voff, wave, lane);
+
+  const int kv_end = CAUSAL ? min(N, i0 + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+  int t_full = N / BC;  // tiles [0, t_full) need no mask
+  if (CAUSAL) t_full = min(t_full, (i0 + 1) / BC);
+  // this wavefront's tiles: [0, t_wave) (causal: up to its own diagonal)
+  const int t_wave = CAUSAL ? min(n_tiles, (wq0 + 31) / BC + 1) : n_tiles;
+
+  // ---- prologue: first K/V tiles in flight, Q tile -> registers (B operand of S^T = K Q^T)
+  if (n_tiles > 0) {
+    load_tile<D, BC, NW>(koff, kh, N, 0, kbuf[0], wave);
+    load_tile<D, BC, NW>(voff, vh, N, 0, vbuf[0], wave);
+  }
+  if (n_tiles > 1) load_tile<D, BC, NW>(koff, kh, N, BC, kbuf[1], wave);
   bf16x8 qreg[KK];
   {
-    const __amdgpu_buffer_rsrc_t qrsrc = buffer_rsrc(qh, (uint32_t)N * D * 2);
+    const __amdgpu_buffer_rsrc_t qrsrc = buffer_rsrc(p.q + head, head_bytes);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       qreg[kk] = __builtin_bit_cast(
           bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (uint32_t)(my_q * D + 16 * kk + 8 * hl) * 2, 0, 0));
   }
 
-  f32x16 oacc[MT];
+  RowState<D> st;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x16{};
-  float m_used = -INFINITY;  // maximum in use, log2 units
-  float l_sum = 0.f;         // this lane's partial row sum (its 16*NC keys per tile)
-  int n_rescale = 0;
-
+  for (int mt = 0; mt < MT; ++mt) st.oacc[mt] = f32x16{};
+  st.m_used = -INFINITY;
+  st.l_sum = 0.f;
+  st.n_rescale = 0;
   const float c = p.c;
   const float tau = p.tau;
 
-  const int kv_end = CAUSAL ? min(N, i0 + BR) : N;
-  const int n_tiles = (kv_end + BC - 1) / BC;
-  int t_full = N / BC;  // tiles [0, t_full) need no mask
-  if (CAUSAL) t_full = min(t_full, (i0 + 1) / BC);
-
-  // ---- K/V staging through registers: thread loads NLD blocks of 4 rows x 16 B
-  u32x4 kst[NLD][4], vst[NLD][4];
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t krsrc = buffer_rsrc(kh, head_bytes);
-  const __amdgpu_buffer_rsrc_t vrsrc = buffer_rsrc(vh, head_bytes);
-  auto gload = [&](int t) {
-    const int j0 = t * BC;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int blk = tid + i * NT;
-      const int col = blk % CPR;
-      const int grp = blk / CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t off = (uint32_t)((j0 + 4 * grp + r) * D + 8 * col) * 2;  // >= head_bytes past N: zeros
-        kst[i][r] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, off, 0, 0);
-        vst[i][r] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0);
-      }
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int blk = tid + i * NT;
-      const int col = blk % CPR;
-      const int grp = blk / CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) *(u32x4*)(ks + (4 * grp + r) * KSTR + 8 * col) = kst[i][r];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) *(u32x4*)(vs + (4 * grp + r) * VSTR + 8 * col) = vst[i][r];
-    }
-  };
-
-  if (n_tiles > 0) gload(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();  // every wave is done reading the previous tile
-    lstore();
-    __syncthreads();
-    if (t + 1 < n_tiles) gload(t + 1);  // next tile's global loads overlap this tile's math
-
-    const int j0 = t * BC;
-    if (CAUSAL && j0 > wq0 + 31) continue;  // whole tile above this wave's diagonal
-    // One instantiation of the tile body for every tile: a second (masked) copy
-    // makes the register allocator shuttle the output accumulators between
-    // register sets on every iteration.
-    tile_step<D, BC, CAUSAL, POLY8, NEG>(ks, vs, qreg, oacc, m_used, l_sum, n_rescale, j0, N, my_q, l32, hl, c, tau,
-                                         t >= t_full);
+  f32x16 sa[NC], sb[NC];
+  __syncthreads();  // K_0, V_0, K_1 resident (the barrier's fence waits for this wave's loads)
+  if (t_wave > 0) {
+    qk_part<D, NC, 0, NC * KK>(kbuf[0], qreg, sa, l32, hl);
   }
 
+  // Iteration t: wait for the loads issued in iteration t-1 (K_{t+1}, V_t), then
+  // refill the buffers freed by iteration t-1: K_{t+2} -> kbuf[t%2] (K_t was read
+  // in iteration t-1) and V_{t+1} -> vbuf[(t+1)%2] (V_{t-1} was read in t-1).
+  auto iteration = [&](int t, f32x16 (&s_cur)[NC], f32x16 (&s_nxt)[NC]) {
+    __syncthreads();
+    if (t + 2 < n_tiles) load_tile<D, BC, NW>(koff, kh, N, (t + 2) * BC, kbuf[t & 1], wave);
+    if (t + 1 < n_tiles) load_tile<D, BC, NW>(voff, vh, N, (t + 1) * BC, vbuf[(t + 1) & 1], wave);
+    if (t < t_wave)  // causal: tiles past this wavefront's diagonal are skipped
+      tile_step<D, BC, CAUSAL, POLY8, NEG>(st, s_cur, s_nxt, qreg, kbuf[(t + 1) & 1], vbuf[t & 1], t >= t_full,
+                                           t * BC, N, my_q, lane, c, tau);
+  };
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    iteration(t, sa, sb);
+    iteration(t + 1, sb, sa);
+  }
+  if (t < n_tiles) iteration(t, sa, sb);
+
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l), written once
-  const float l_tot = pair_sum(l_sum);
+  const float l_tot = pair_sum(st.l_sum);
   if (my_q < N) {
     const float inv = 1.f / l_tot;
     const size_t row = (size_t)bh * N + my_q;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dv = 32 * mt + 8 * g + 4 * hl;
+      for (int gq = 0; gq < 4; ++gq) {
+        const int dv = 32 * mt + 8 * gq + 4 * hl;
         if (OF32) {
           f32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = oacc[mt][4 * g + e] * inv;
+          for (int e = 0; e < 4; ++e) w[e] = st.oacc[mt][4 * gq + e] * inv;
           *(f32x4*)((float*)p.o + row * D + dv) = w;
         } else {
           bf16x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[mt][4 * g + e] * inv);
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.oacc[mt][4 * gq + e] * inv);
           *(bf16x4*)((__bf16*)p.o + row * D + dv) = w;
         }
       }
     if (hl == 0) {
-      p.lse[row] = 0.69314718055994531f * (m_used + log2f(l_tot));
-      if (p.rescale_count) p.rescale_count[row] = n_rescale;
+      p.lse[row] = 0.69314718055994531f * (st.m_used + log2f(l_tot));
+      if (p.rescale_count) p.rescale_count[row] = st.n_rescale;
     }
   }
 }

@@ -121,6 +121,12 @@ attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const 
                              const float* lse, int B, int H, int N, int d, int causal,
                              float scale, const attn_fwd_opts* opts);
 
+/* Tile shape the kernel uses for head dim d: query rows per workgroup and keys
+ * per KV tile (the granularity of the online softmax and of the rescale
+ * decisions, which the optional rescale counter reports). Returns ATTN_OK, or
+ * ATTN_ERR_UNSUPPORTED for a head dim other than 64 or 128, or ATTN_ERR_NULL. */
+attn_status_t attn_fwd_tile_shape(int d, int* query_rows, int* key_cols);
+
 /* Static text for a status code. */
 const char* attn_status_str(attn_status_t status);
 

@@ -95,6 +95,12 @@ def test_options():
     assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(rescale_count=6 * GB)) == bnd.ATTN_OK
 
 
+def test_tile_shape():
+    assert bnd.tile_shape(128)[0] % 32 == 0 and bnd.tile_shape(64)[1] % 32 == 0
+    with pytest.raises(bnd.AttnError):
+        bnd.tile_shape(96)
+
+
 def test_status_strings():
     lib = bnd.lib()
     for code in range(9):

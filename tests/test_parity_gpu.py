@@ -160,8 +160,8 @@ def test_rescale_counts_follow_the_threshold():
     _, _, c8 = run_gpu(q, k, v, True, s, tau=8.0, rescale_count=True)
     note(f"  rescales: tau=0 {int(c0.sum())}  tau=8 {int(c8.sum())}")
     assert c0.sum() >= 10 * max(1, c8.sum())
-    _, _, m0 = oracle.tiled_online_attention(q, k, v, True, s, 128, 128, 0.0)
-    # the model uses the same tiling as the d=64 kernel (128 query rows, 128-key tiles)
+    br, bc = binding.tile_shape(64)   # the model uses the kernel's tiling
+    _, _, m0 = oracle.tiled_online_attention(q, k, v, True, s, br, bc, 0.0)
     agree = np.mean(c0 == m0)
     note(f"  per-row agreement with fp64 model (tau=0): {agree:.4f}")
     assert agree >= 0.99
