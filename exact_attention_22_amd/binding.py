@@ -13,7 +13,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
+# EXACT_ATTN_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("EXACT_ATTN_LIB") or os.path.join(_PKG, "libattn_fwd.so")
 
 ATTN_OK = 0
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_DIM", 3: "ATTN_ERR_UNSUPPORTED",

@@ -145,15 +145,29 @@ __device__ __forceinline__ bf16x8 k_frag(const char* kb, int R, int c) {
   return *(const bf16x8*)(kb + R * (2 * D) + ((c ^ kswz<D>(R)) << 4));
 }
 
-// Four consecutive keys (rows row0 + e, e = 0..3) of value feature col0 + (lane % 16)
-// from the swizzled V tile, by the LDS transpose read.
+// Transpose-read addressing of the swizzled V tile. For value-feature block mt,
+// lane l (16-lane group g, index i) reads key rows row0 + i/4 with
+// row0 = 32*cc + 16*h + 4*(g/2) (+ 8 for the second read) and value features
+// 32*mt + 16*(g%2) + 4*(i%4) .. +3. The swizzle only depends on the row modulo 4
+// (D = 128) or 4 (D = 64: (row/2)%2), which cc, h and the +8 do not change, so
+// the byte offset is a per-lane part (v_offsets, once per kernel) plus a
+// compile-time row offset folded into the instruction.
 template <int D>
-__device__ __forceinline__ s16x4 v_col4(const char* vb, int row0, int col0, int lane) {
-  const int i = lane & 15;
-  const int r = row0 + (i >> 2);
-  const int dv = col0 + 4 * (i & 3);
-  const char* p = vb + r * (2 * D) + (((dv >> 3) ^ vswz<D>(r)) << 4) + ((dv & 7) << 1);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_void*)p);
+__device__ __forceinline__ void v_offsets(int (&voffs)[D / 32], int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const int r = 4 * (g >> 1) + (i >> 2);  // row within a 16-row block
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) {
+    const int dv = 32 * mt + 16 * (g & 1) + 4 * (i & 3);
+    voffs[mt] = r * (2 * D) + (((dv >> 3) ^ vswz<D>(r)) << 4) + ((dv & 7) << 1);
+  }
+}
+// Four consecutive keys of one value feature (see v_offsets); `rows` is the
+// compile-time row offset 32*cc + 16*h (+8).
+template <int D>
+__device__ __forceinline__ s16x4 v_col4(const char* vrow, int rows) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(lds_void*)(vrow + rows * (2 * D)));
 }
 
 // Max / min / sum of a value with its copy in lane l^32 (the other half of the same query row).
@@ -191,6 +205,7 @@ template <int D>
 struct RowState {
   f32x16 oacc[D / 32];  // O^T accumulator (unnormalised)
   float m_used;          // maximum in use, log2 units
+  float thr;             // m_used + tau: a tile maximum above it triggers a rescale
   float l_sum;           // this lane's partial row sum
   int n_rescale;
 };
@@ -201,11 +216,13 @@ struct RowState {
 template <int D, int BC, bool CAUSAL, int POLY8, bool NEG>
 __device__ __forceinline__ void tile_step(RowState<D>& st, f32x16 (&s_cur)[BC / 32], f32x16 (&s_nxt)[BC / 32],
                                           const bf16x8 (&qreg)[D / 16], const char* kb_nxt, const char* vb_cur,
-                                          bool masked, int j0, int N, int my_q, int lane, float c, float tau) {
+                                          const int (&voffs)[D / 32], bool masked, int j0, int N, int my_q, int lane,
+                                          float c, float tau) {
+  // (a row's first tile always holds a visible key - key 0 - so m_tile is finite there)
   constexpr int NC = BC / 32;
   constexpr int MT = D / 32;
   constexpr float mask_val = NEG ? INFINITY : -INFINITY;
-  const int l32 = lane & 31, hl = lane >> 5, g = lane >> 4;
+  const int l32 = lane & 31, hl = lane >> 5;
 
   // First half of the next tile's scores: independent of this tile's softmax.
   // Computed unconditionally (past the last tile, or past a causal wavefront's
@@ -234,13 +251,14 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, f32x16 (&s_cur)[BC / 
   red = NEG ? pair_min(red) : pair_max(red);
   const float m_tile = red * c;  // -inf when every key of the row is masked (c is never 0)
 
-  // ---- adaptive rescale: only when the maximum grows by more than tau
-  const float m_new = fmaxf(st.m_used, m_tile);
-  const bool need = (m_new - st.m_used) > tau;  // +inf on the row's first tile; NaN (false) if both -inf
+  // ---- adaptive rescale: only when the tile maximum exceeds the maximum in use
+  //      by more than tau (st.thr = m_used + tau; -inf before the row's first tile)
+  const bool need = m_tile > st.thr;
   if (__any(need)) {
-    const float alpha = need ? __builtin_amdgcn_exp2f(st.m_used - m_new) : 1.f;
+    const float alpha = need ? __builtin_amdgcn_exp2f(st.m_used - m_tile) : 1.f;
     st.n_rescale += (need && st.m_used != -INFINITY) ? 1 : 0;
-    st.m_used = need ? m_new : st.m_used;
+    st.m_used = need ? m_tile : st.m_used;
+    st.thr = st.m_used + tau;
     st.l_sum *= alpha;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -254,6 +272,9 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, f32x16 (&s_cur)[BC / 
   // ---- P = 2^(s*c - m), row sum in fp32, bf16 pack in the PV operand order;
   //      O^T += V^T P^T per 16-key step as soon as its P fragment is packed
   const float mc = -st.m_used;
+  const char* vrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) vrow[mt] = vb_cur + voffs[mt];
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
 #pragma unroll
@@ -271,12 +292,10 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, f32x16 (&s_cur)[BC / 
         st.l_sum += e;
         pb[j] = (__bf16)e;
       }
-      const int row0 = 32 * cc + 16 * h + 4 * (g >> 1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int col0 = 32 * mt + 16 * (g & 1);
-        const s16x4 lo = v_col4<D>(vb_cur, row0, col0, lane);
-        const s16x4 hi = v_col4<D>(vb_cur, row0 + 8, col0, lane);
+        const s16x4 lo = v_col4<D>(vrow[mt], 32 * cc + 16 * h);
+        const s16x4 hi = v_col4<D>(vrow[mt], 32 * cc + 16 * h + 8);
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         st.oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, st.oacc[mt], 0, 0, 0);
       }
@@ -315,7 +334,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases stay scalar
   const int l32 = lane & 31;
   const int hl = lane >> 5;
   const int wq0 = i0 + wave * 32;
@@ -327,6 +346,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
   uint32_t koff[LPW], voff[LPW];
   load_offsets<D, BC, NW, true>(koff, wave, lane);
   load_offsets<D, BC, NW, false>(voff, wave, lane);
+  int voffs[MT];
+  v_offsets<D>(voffs, lane);
 
   const int kv_end = CAUSAL ? min(N, i0 + BR) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
@@ -354,6 +375,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) st.oacc[mt] = f32x16{};
   st.m_used = -INFINITY;
+  st.thr = -INFINITY;
   st.l_sum = 0.f;
   st.n_rescale = 0;
   const float c = p.c;
@@ -373,8 +395,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
     if (t + 2 < n_tiles) load_tile<D, BC, NW>(koff, kh, N, (t + 2) * BC, kbuf[t & 1], wave);
     if (t + 1 < n_tiles) load_tile<D, BC, NW>(voff, vh, N, (t + 1) * BC, vbuf[(t + 1) & 1], wave);
     if (t < t_wave)  // causal: tiles past this wavefront's diagonal are skipped
-      tile_step<D, BC, CAUSAL, POLY8, NEG>(st, s_cur, s_nxt, qreg, kbuf[(t + 1) & 1], vbuf[t & 1], t >= t_full,
-                                           t * BC, N, my_q, lane, c, tau);
+      tile_step<D, BC, CAUSAL, POLY8, NEG>(st, s_cur, s_nxt, qreg, kbuf[(t + 1) & 1], vbuf[t & 1], voffs,
+                                           t >= t_full, t * BC, N, my_q, lane, c, tau);
   };
   int t = 0;
   for (; t + 1 < n_tiles; t += 2) {
