@@ -292,6 +292,11 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, f32x16 (&s_cur)[BC / 
         st.l_sum += e;
         pb[j] = (__bf16)e;
       }
+      // A wavefront's own loads into LDS must have landed before it issues LDS
+      // transpose reads (observed on MI355X: without this wait the transpose
+      // reads return wrong data although the loads in flight target other
+      // buffers; other wavefronts' loads in flight are harmless). vmcnt(0) only.
+      if (cc == 0 && h == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const s16x4 lo = v_col4<D>(vrow[mt], 32 * cc + 16 * h);
@@ -313,10 +318,13 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert(POLY8 == 0 || POLY8 == 4 || POLY8 == 8, "poly split");
 
-  // K tile buffers 0,1 then V tile buffers 0,1
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
-  char* const kbuf[2] = {smem, smem + TILEB};
-  char* const vbuf[2] = {smem + 2 * TILEB, smem + 3 * TILEB};
+  // Double-buffered K and V tiles as four separate LDS objects: the compiler
+  // then knows that reads of one buffer do not alias the loads in flight into
+  // another, and does not wait for those loads before each read.
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TILEB];
 
   // ---- work decomposition: workgroups are dealt round-robin to the 8 XCDs, so
   // give XCD x the contiguous slice [x*per_xcd, (x+1)*per_xcd) of tiles: the
@@ -358,10 +366,10 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
 
   // ---- prologue: first K/V tiles in flight, Q tile -> registers (B operand of S^T = K Q^T)
   if (n_tiles > 0) {
-    load_tile<D, BC, NW>(koff, kh, N, 0, kbuf[0], wave);
-    load_tile<D, BC, NW>(voff, vh, N, 0, vbuf[0], wave);
+    load_tile<D, BC, NW>(koff, kh, N, 0, kbuf0, wave);
+    load_tile<D, BC, NW>(voff, vh, N, 0, vbuf0, wave);
   }
-  if (n_tiles > 1) load_tile<D, BC, NW>(koff, kh, N, BC, kbuf[1], wave);
+  if (n_tiles > 1) load_tile<D, BC, NW>(koff, kh, N, BC, kbuf1, wave);
   bf16x8 qreg[KK];
   {
     const __amdgpu_buffer_rsrc_t qrsrc = buffer_rsrc(p.q + head, head_bytes);
@@ -384,26 +392,29 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
   f32x16 sa[NC], sb[NC];
   __syncthreads();  // K_0, V_0, K_1 resident (the barrier's fence waits for this wave's loads)
   if (t_wave > 0) {
-    qk_part<D, NC, 0, NC * KK>(kbuf[0], qreg, sa, l32, hl);
+    qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, sa, l32, hl);
   }
 
   // Iteration t: wait for the loads issued in iteration t-1 (K_{t+1}, V_t), then
   // refill the buffers freed by iteration t-1: K_{t+2} -> kbuf[t%2] (K_t was read
   // in iteration t-1) and V_{t+1} -> vbuf[(t+1)%2] (V_{t-1} was read in t-1).
-  auto iteration = [&](int t, f32x16 (&s_cur)[NC], f32x16 (&s_nxt)[NC]) {
+  // (t even: K_t in kbuf0, V_t in vbuf0; t odd: kbuf1, vbuf1; the buffers are
+  // picked at compile time in the two halves of the unrolled loop.)
+  auto iteration = [&](int t, f32x16 (&s_cur)[NC], f32x16 (&s_nxt)[NC], char* kb_t, char* kb_t1, char* vb_t,
+                       char* vb_t1) {
     __syncthreads();
-    if (t + 2 < n_tiles) load_tile<D, BC, NW>(koff, kh, N, (t + 2) * BC, kbuf[t & 1], wave);
-    if (t + 1 < n_tiles) load_tile<D, BC, NW>(voff, vh, N, (t + 1) * BC, vbuf[(t + 1) & 1], wave);
+    if (t + 2 < n_tiles) load_tile<D, BC, NW>(koff, kh, N, (t + 2) * BC, kb_t, wave);
+    if (t + 1 < n_tiles) load_tile<D, BC, NW>(voff, vh, N, (t + 1) * BC, vb_t1, wave);
     if (t < t_wave)  // causal: tiles past this wavefront's diagonal are skipped
-      tile_step<D, BC, CAUSAL, POLY8, NEG>(st, s_cur, s_nxt, qreg, kbuf[(t + 1) & 1], vbuf[t & 1], voffs,
-                                           t >= t_full, t * BC, N, my_q, lane, c, tau);
+      tile_step<D, BC, CAUSAL, POLY8, NEG>(st, s_cur, s_nxt, qreg, kb_t1, vb_t, voffs, t >= t_full, t * BC, N, my_q,
+                                           lane, c, tau);
   };
   int t = 0;
   for (; t + 1 < n_tiles; t += 2) {
-    iteration(t, sa, sb);
-    iteration(t + 1, sb, sa);
+    iteration(t, sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
+    iteration(t + 1, sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
   }
-  if (t < n_tiles) iteration(t, sa, sb);
+  if (t < n_tiles) iteration(t, sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l), written once
   const float l_tot = pair_sum(st.l_sum);
