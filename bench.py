@@ -13,6 +13,7 @@ bounded sample of the same workload (cpu_baseline).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -25,6 +26,30 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "exact_attention_22_amd", "csrc")
+KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip", "exp2_poly.h")
+
+# HBM bytes per launch of the headline kernel from two rocprofv3 --pmc runs
+# (FETCH_SIZE and WRITE_SIZE, KiB per dispatch), each scaled by what the same
+# counter reads for a 256 MiB device copy (FETCH x2.0, WRITE x1.0); see
+# profiles/attn_fwd_headline_counters.md. Valid only for the kernel sources
+# with this SHA-256; any change to them reports traffic as null.
+TRAFFIC = {"sources_sha256": "b6fc89f47d98c4506656508a9b6b524b6c11a8fbe456cb3a8094daec2ba65ab3",
+           "fetch_kib": 198100.0, "write_kib": 137200.0, "fetch_scale": 2.0, "write_scale": 1.0}
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(workload_name: str):
+    if workload_name != "headline" or kernel_sources_sha256() != TRAFFIC["sources_sha256"]:
+        return None
+    return int((TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"] + TRAFFIC["write_kib"] * TRAFFIC["write_scale"]) * 1024)
 
 
 def parse():
@@ -153,7 +178,8 @@ def main():
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal},
         "frac_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_bytes(w.name)},
         "timed_wall_s": round(wall, 2),
         "workloads": others,
     }

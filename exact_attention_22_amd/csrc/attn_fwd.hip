@@ -34,12 +34,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Tile configuration per head dim: (BC keys per tile, NW waves per workgroup).
-constexpr int kWaves = 4;
+// Tile configuration: 8 wavefronts (256 query rows) per workgroup, BC keys per KV tile.
+constexpr int kWaves = 8;
 constexpr int kRows = 32 * kWaves;  // query rows per workgroup
 template <int D> struct Cfg;
-template <> struct Cfg<128> { static constexpr int BC = 32; };
-template <> struct Cfg<64> { static constexpr int BC = 32; };
+template <> struct Cfg<128> { static constexpr int BC = 64; };
+template <> struct Cfg<64> { static constexpr int BC = 64; };
 
 template <int D, bool CAUSAL, bool OF32, int POLY8>
 hipError_t launch(const attn::Params& p, bool neg, hipStream_t stream) {
@@ -47,8 +47,8 @@ hipError_t launch(const attn::Params& p, bool neg, hipStream_t stream) {
   // A negative scale flips the row maximum of s*c into c * min(s): separate instantiation.
   const dim3 grid(p.per_xcd * 8), block(64 * kWaves);
   void* args[] = {const_cast<attn::Params*>(&p)};
-  const void* fn = neg ? reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, kWaves, CAUSAL, OF32, POLY8, true>)
-                       : reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, kWaves, CAUSAL, OF32, POLY8, false>);
+  const void* fn = neg ? reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, OF32, POLY8, true>)
+                       : reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, OF32, POLY8, false>);
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

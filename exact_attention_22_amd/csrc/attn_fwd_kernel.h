@@ -1,7 +1,7 @@
 // attn_fwd_kernel.h - tiled exact-attention forward kernel for gfx950 (MI355X).
 //
-// One workgroup computes BR = 32*NW query rows of one (batch, head); each of
-// its NW wavefronts owns 32 rows. The keys and values stream through LDS in
+// One workgroup computes 256 query rows of one (batch, head); each of its 8
+// wavefronts owns 32 rows. The keys and values stream through LDS in
 // tiles of BC rows, the queries stay in registers, and per query row the kernel
 // keeps a running maximum and running sum, so the N x N score matrix never
 // leaves the chip (page "Flash Attention" glossary, sections "Tiling with SRAM"
@@ -30,14 +30,20 @@
 //
 // Data movement: K and V tiles go from HBM/L2 straight into LDS with buffer
 // loads that write LDS (each wave instruction fills 1 KiB: lane l's 16 bytes
-// land at base + 16*l), double-buffered, one barrier per tile. Rows are stored
+// land at base + 16*l), double-buffered. Rows are stored
 // unpadded with an XOR swizzle of their 16-byte chunks, chosen so that both the
 // 16-byte K reads and the V transpose reads are free of bank conflicts. Keys
 // past N read as zeros (buffer range check) and are masked.
 //
-// Software pipeline per wavefront: while the softmax of tile t runs on the
-// VALU, the matrix cores compute S for tile t+1; then O += P_t V_t. The loop is
-// unrolled by two so the two score buffers swap roles without register copies.
+// Schedule: a workgroup holds two groups of four wavefronts (one of each per
+// SIMD) that alternate, one phase apart, between the softmax of tile t on the
+// VALU and the matrix work (O += P_t V_t, S_{t+1} = K_{t+1} Q^T), so every SIMD
+// keeps one wavefront feeding the matrix core while the other computes
+// exponentials (see the ping-pong section below). This is the CDNA form of the
+// overlap the pages obtain with warp specialisation and asynchronous MMA (page
+// "FlashAttention 4: faster, more memory-efficient attention for LLMs",
+// section "What's new in FlashAttention 4"; page "FlashAttention-4:
+// algorithm-kernel fused pipeline for asymmetric hardware scaling", section 2).
 //
 // Online softmax with the adaptive rescale of page "FlashAttention 4: faster,
 // more memory-efficient attention for LLMs", section "Smarter online softmax
@@ -210,27 +216,39 @@ struct RowState {
   int n_rescale;
 };
 
-// One KV tile for a wavefront, software-pipelined: the softmax of tile t (scores
-// in s_cur) overlaps the S^T MFMAs of tile t+1 (into s_nxt, K tile in kb_nxt),
-// then O^T += V_t^T P_t^T with V_t in vb_cur.
+// ============================================================================
+// Ping-pong schedule: one workgroup of 8 wavefronts (two per SIMD, 256 query
+// rows). Group A (wavefronts 0-3) and group B (4-7) run the same per-tile
+// sequence - a VALU phase (softmax of tile t: S_t -> P_t) and a matrix phase
+// (O += P_t V_t, then S_{t+1} = K_{t+1} Q^T) - offset by one phase, with a
+// workgroup barrier between phases. Wavefronts are dealt to the SIMDs
+// round-robin, so every SIMD holds one wavefront of each group and always has
+// one of them feeding the matrix core while the other runs the softmax.
+//
+// Global step 2k:   A: softmax(k)          B: matrix(k-1)
+// Global step 2k+1: A: matrix(k)           B: loads K_{k+2}, V_{k+1}; softmax(k)
+// Group B issues every tile load during its softmax phase and waits for them
+// at the start of its next matrix phase, before its LDS transpose reads; group
+// A never has loads of its own in flight.
+// ============================================================================
+
+// Barrier between phases that orders LDS only: it waits for this wavefront's
+// LDS reads and writes, not for its global->LDS loads in flight.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// VALU phase: mask (boundary tiles), tile maximum, adaptive rescale,
+// P = 2^(s*c - m) with the fp32 row sum, packed to bf16 in the PV operand order.
 template <int D, int BC, bool CAUSAL, int POLY8, bool NEG>
-__device__ __forceinline__ void tile_step(RowState<D>& st, f32x16 (&s_cur)[BC / 32], f32x16 (&s_nxt)[BC / 32],
-                                          const bf16x8 (&qreg)[D / 16], const char* kb_nxt, const char* vb_cur,
-                                          const int (&voffs)[D / 32], bool masked, int j0, int N, int my_q, int lane,
-                                          float c, float tau) {
-  // (a row's first tile always holds a visible key - key 0 - so m_tile is finite there)
+__device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 32][2],
+                                              bool masked, int j0, int N, int my_q, int lane, float c, float tau) {
   constexpr int NC = BC / 32;
   constexpr int MT = D / 32;
   constexpr float mask_val = NEG ? INFINITY : -INFINITY;
-  const int l32 = lane & 31, hl = lane >> 5;
-
-  // First half of the next tile's scores: independent of this tile's softmax.
-  // Computed unconditionally (past the last tile, or past a causal wavefront's
-  // diagonal, the result is unused): straight-line code keeps the two score
-  // buffers in place.
-  qk_part<D, NC, 0, NC * (D / 16) / 2>(kb_nxt, qreg, s_nxt, l32, hl);
-
-  // ---- mask: keys past N, and (causal) keys after the query; boundary tiles only
+  const int hl = lane >> 5;
   if (masked) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
@@ -238,21 +256,16 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, f32x16 (&s_cur)[BC / 
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 32 * cc + 8 * (r / 4) + 4 * hl + (r % 4);
         const bool hide = key >= N || (CAUSAL && key > my_q);
-        s_cur[cc][r] = hide ? mask_val : s_cur[cc][r];
+        s[cc][r] = hide ? mask_val : s[cc][r];
       }
   }
-
-  // ---- tile row maximum of s*c: in-lane, then the lane pair
-  float red = s_cur[0][0];
+  float red = s[0][0];
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red = NEG ? fminf(red, s_cur[cc][r]) : fmaxf(red, s_cur[cc][r]);
+    for (int r = 0; r < 16; ++r) red = NEG ? fminf(red, s[cc][r]) : fmaxf(red, s[cc][r]);
   red = NEG ? pair_min(red) : pair_max(red);
   const float m_tile = red * c;  // -inf when every key of the row is masked (c is never 0)
-
-  // ---- adaptive rescale: only when the tile maximum exceeds the maximum in use
-  //      by more than tau (st.thr = m_used + tau; -inf before the row's first tile)
   const bool need = m_tile > st.thr;
   if (__any(need)) {
     const float alpha = need ? __builtin_amdgcn_exp2f(st.m_used - m_tile) : 1.f;
@@ -265,70 +278,69 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, f32x16 (&s_cur)[BC / 
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.oacc[mt][r] *= alpha;
   }
-
-  // ---- second half of the next tile's scores
-  qk_part<D, NC, NC * (D / 16) / 2, NC * (D / 16)>(kb_nxt, qreg, s_nxt, l32, hl);
-
-  // ---- P = 2^(s*c - m), row sum in fp32, bf16 pack in the PV operand order;
-  //      O^T += V^T P^T per 16-key step as soon as its P fragment is packed
   const float mc = -st.m_used;
-  const char* vrow[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) vrow[mt] = vb_cur + voffs[mt];
+  for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 pb;
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = 8 * h + j;
-        const float x = fmaf(s_cur[cc][r], c, mc);
+        const float x = fmaf(s[cc][r], c, mc);
         float e;
         if (POLY8 == 8 || (POLY8 == 4 && (r & 4)))
           e = attn_exp2_poly(x);
         else
           e = __builtin_amdgcn_exp2f(x);
         st.l_sum += e;
-        pb[j] = (__bf16)e;
+        pb[cc][h][j] = (__bf16)e;
       }
-      // A wavefront's own loads into LDS must have landed before it issues LDS
-      // transpose reads (observed on MI355X: without this wait the transpose
-      // reads return wrong data although the loads in flight target other
-      // buffers; other wavefronts' loads in flight are harmless). vmcnt(0) only.
-      if (cc == 0 && h == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Matrix phase: O^T += V_t^T P_t^T (V_t in vb), then S = K_{t+1} Q^T (K_{t+1} in kb).
+template <int D, int BC>
+__device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 32], const bf16x8 (&pb)[BC / 32][2],
+                                             const bf16x8 (&qreg)[D / 16], const char* kb, const char* vb,
+                                             const int (&voffs)[D / 32], bool do_qk, int lane) {
+  constexpr int NC = BC / 32;
+  constexpr int MT = D / 32;
+  const int l32 = lane & 31, hl = lane >> 5;
+  // Issue priority up while this wavefront feeds the matrix core, so the
+  // softmax wavefront on the same SIMD does not delay its MFMA issue.
+  __builtin_amdgcn_s_setprio(1);
+  const char* vrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) vrow[mt] = vb + voffs[mt];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const s16x4 lo = v_col4<D>(vrow[mt], 32 * cc + 16 * h);
         const s16x4 hi = v_col4<D>(vrow[mt], 32 * cc + 16 * h + 8);
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        st.oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, st.oacc[mt], 0, 0, 0);
+        st.oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc][h], st.oacc[mt], 0, 0, 0);
       }
-    }
-  }
+  if (do_qk) qk_part<D, NC, 0, NC * (D / 16)>(kb, qreg, s, l32, hl);
+  __builtin_amdgcn_s_setprio(0);
 }
 
-template <int D, int BC, int NW, bool CAUSAL, bool OF32, int POLY8, bool NEG>
-__global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
+template <int D, int BC, bool CAUSAL, bool OF32, int POLY8, bool NEG>
+__global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
+  constexpr int NW = 8;            // wavefronts per workgroup (2 per SIMD)
   constexpr int BR = 32 * NW;      // query rows per workgroup
-  constexpr int NC = BC / 32;      // 32-key chunks per KV tile
-  constexpr int KK = D / 16;       // k-steps of S^T = K Q^T
-  constexpr int MT = D / 32;       // 32-row blocks of O^T
+  constexpr int NC = BC / 32;
+  constexpr int KK = D / 16;
+  constexpr int MT = D / 32;
   constexpr int TILEB = BC * D * 2;
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert(POLY8 == 0 || POLY8 == 4 || POLY8 == 8, "poly split");
 
-  // Double-buffered K and V tiles as four separate LDS objects: the compiler
-  // then knows that reads of one buffer do not alias the loads in flight into
-  // another, and does not wait for those loads before each read.
   __shared__ __attribute__((aligned(1024))) char kbuf0[TILEB];
   __shared__ __attribute__((aligned(1024))) char kbuf1[TILEB];
   __shared__ __attribute__((aligned(1024))) char vbuf0[TILEB];
   __shared__ __attribute__((aligned(1024))) char vbuf1[TILEB];
 
-  // ---- work decomposition: workgroups are dealt round-robin to the 8 XCDs, so
-  // give XCD x the contiguous slice [x*per_xcd, (x+1)*per_xcd) of tiles: the
-  // q-tiles of one head then share that XCD's L2 for their K/V re-reads.
   const int wg = blockIdx.x;
   const int logical = (wg & 7) * p.per_xcd + (wg >> 3);
   if (logical >= p.total_tiles) return;
@@ -342,34 +354,35 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: group A, 1: group B
   const int l32 = lane & 31;
   const int hl = lane >> 5;
   const int wq0 = i0 + wave * 32;
-  const int my_q = wq0 + l32;  // the query row this lane owns
+  const int my_q = wq0 + l32;
 
   const __bf16* const kh = p.k + head;
   const __bf16* const vh = p.v + head;
-  constexpr int LPW = LoadShape<D, BC, NW>::LPW;
+  constexpr int LPW = LoadShape<D, BC, 4>::LPW;  // group B's four wavefronts load every tile
   uint32_t koff[LPW], voff[LPW];
-  load_offsets<D, BC, NW, true>(koff, wave, lane);
-  load_offsets<D, BC, NW, false>(voff, wave, lane);
+  load_offsets<D, BC, 4, true>(koff, wave & 3, lane);
+  load_offsets<D, BC, 4, false>(voff, wave & 3, lane);
   int voffs[MT];
   v_offsets<D>(voffs, lane);
 
   const int kv_end = CAUSAL ? min(N, i0 + BR) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
-  int t_full = N / BC;  // tiles [0, t_full) need no mask
+  int t_full = N / BC;
   if (CAUSAL) t_full = min(t_full, (i0 + 1) / BC);
-  // this wavefront's tiles: [0, t_wave) (causal: up to its own diagonal)
   const int t_wave = CAUSAL ? min(n_tiles, (wq0 + 31) / BC + 1) : n_tiles;
 
-  // ---- prologue: first K/V tiles in flight, Q tile -> registers (B operand of S^T = K Q^T)
-  if (n_tiles > 0) {
-    load_tile<D, BC, NW>(koff, kh, N, 0, kbuf0, wave);
-    load_tile<D, BC, NW>(voff, vh, N, 0, vbuf0, wave);
+  if (grp == 1) {
+    if (n_tiles > 0) {
+      load_tile<D, BC, 4>(koff, kh, N, 0, kbuf0, wave & 3);
+      load_tile<D, BC, 4>(voff, vh, N, 0, vbuf0, wave & 3);
+    }
+    if (n_tiles > 1) load_tile<D, BC, 4>(koff, kh, N, BC, kbuf1, wave & 3);
   }
-  if (n_tiles > 1) load_tile<D, BC, NW>(koff, kh, N, BC, kbuf1, wave);
   bf16x8 qreg[KK];
   {
     const __amdgpu_buffer_rsrc_t qrsrc = buffer_rsrc(p.q + head, head_bytes);
@@ -378,7 +391,6 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
       qreg[kk] = __builtin_bit_cast(
           bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (uint32_t)(my_q * D + 16 * kk + 8 * hl) * 2, 0, 0));
   }
-
   RowState<D> st;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) st.oacc[mt] = f32x16{};
@@ -389,34 +401,47 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const Params p) {
   const float c = p.c;
   const float tau = p.tau;
 
-  f32x16 sa[NC], sb[NC];
-  __syncthreads();  // K_0, V_0, K_1 resident (the barrier's fence waits for this wave's loads)
-  if (t_wave > 0) {
-    qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, sa, l32, hl);
+  f32x16 s[NC];
+  bf16x8 pb[NC][2];
+  __syncthreads();  // K_0, V_0, K_1 resident
+  if (t_wave > 0) qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, s, l32, hl);
+
+  // Pairs of global steps (2k, 2k+1), k = 0 .. n_tiles; kb0/vb0 hold the tiles of
+  // k's parity. The two groups run separate straight loops with the same number
+  // of barriers (two per pair).
+  if (grp == 0) {
+    auto pair = [&](int k, char* kb1, char* vb0) {
+      if (k < t_wave) softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, k * BC, N, my_q, lane, c, tau);
+      phase_barrier();
+      if (k < t_wave) matrix_phase<D, BC>(st, s, pb, qreg, kb1, vb0, voffs, k + 1 < t_wave, lane);
+      phase_barrier();
+    };
+    int k = 0;
+    for (; k + 1 <= n_tiles; k += 2) {
+      pair(k, kbuf1, vbuf0);
+      pair(k + 1, kbuf0, vbuf1);
+    }
+    if (k <= n_tiles) pair(k, kbuf1, vbuf0);
+  } else {
+    auto pair = [&](int k, char* kb0, char* vb1) {
+      if (k >= 1 && k - 1 < t_wave) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // own loads landed before the transpose reads (vmcnt(0))
+        matrix_phase<D, BC>(st, s, pb, qreg, kb0, vb1, voffs, k < t_wave, lane);
+      }
+      phase_barrier();
+      if (k + 2 < n_tiles) load_tile<D, BC, 4>(koff, kh, N, (k + 2) * BC, kb0, wave & 3);
+      if (k + 1 < n_tiles) load_tile<D, BC, 4>(voff, vh, N, (k + 1) * BC, vb1, wave & 3);
+      if (k < t_wave) softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, k * BC, N, my_q, lane, c, tau);
+      phase_barrier();
+    };
+    int k = 0;
+    for (; k + 1 <= n_tiles; k += 2) {
+      pair(k, kbuf0, vbuf1);
+      pair(k + 1, kbuf1, vbuf0);
+    }
+    if (k <= n_tiles) pair(k, kbuf0, vbuf1);
   }
 
-  // Iteration t: wait for the loads issued in iteration t-1 (K_{t+1}, V_t), then
-  // refill the buffers freed by iteration t-1: K_{t+2} -> kbuf[t%2] (K_t was read
-  // in iteration t-1) and V_{t+1} -> vbuf[(t+1)%2] (V_{t-1} was read in t-1).
-  // (t even: K_t in kbuf0, V_t in vbuf0; t odd: kbuf1, vbuf1; the buffers are
-  // picked at compile time in the two halves of the unrolled loop.)
-  auto iteration = [&](int t, f32x16 (&s_cur)[NC], f32x16 (&s_nxt)[NC], char* kb_t, char* kb_t1, char* vb_t,
-                       char* vb_t1) {
-    __syncthreads();
-    if (t + 2 < n_tiles) load_tile<D, BC, NW>(koff, kh, N, (t + 2) * BC, kb_t, wave);
-    if (t + 1 < n_tiles) load_tile<D, BC, NW>(voff, vh, N, (t + 1) * BC, vb_t1, wave);
-    if (t < t_wave)  // causal: tiles past this wavefront's diagonal are skipped
-      tile_step<D, BC, CAUSAL, POLY8, NEG>(st, s_cur, s_nxt, qreg, kb_t1, vb_t, voffs, t >= t_full, t * BC, N, my_q,
-                                           lane, c, tau);
-  };
-  int t = 0;
-  for (; t + 1 < n_tiles; t += 2) {
-    iteration(t, sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
-    iteration(t + 1, sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
-  }
-  if (t < n_tiles) iteration(t, sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
-
-  // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l), written once
   const float l_tot = pair_sum(st.l_sum);
   if (my_q < N) {
     const float inv = 1.f / l_tot;
