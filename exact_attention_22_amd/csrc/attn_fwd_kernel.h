@@ -62,6 +62,7 @@
 
 #include "exp2_poly.h"
 
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -135,11 +136,15 @@ __device__ __forceinline__ void load_offsets(uint32_t* off, int wave, int lane) 
   }
 }
 
+// A tile that is not `live` (past the last tile) gets a zero-size resource: its
+// loads fill the buffer with zeros without touching memory, so every step issues
+// the same loads and the load/wait sequence has no branches.
 template <int D, int BC, int NW>
 __device__ __forceinline__ void load_tile(const uint32_t* off, const __bf16* head, int N, int j0, char* buf,
-                                          int wave) {
+                                          int wave, bool live) {
   using S = LoadShape<D, BC, NW>;
-  const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(head + (size_t)j0 * D, (uint32_t)(N - j0) * D * 2);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      buffer_rsrc(head + (size_t)(live ? j0 : 0) * D, live ? (uint32_t)(N - j0) * D * 2 : 0u);
 #pragma unroll
   for (int i = 0; i < S::LPW; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(buf + (wave * S::LPW + i) * 1024), 16, off[i], 0, 0, 0);
@@ -206,6 +211,21 @@ __device__ __forceinline__ void qk_part(const char* kb, const bf16x8 (&qreg)[D /
   }
 }
 
+// PV operands (V^T fragments) of k-steps [G0, G1): k-step g = 2*cc + h covers
+// keys 32*cc + 16*h .. +15; one fragment per value-feature block mt.
+template <int D, int BC, int G0, int G1>
+__device__ __forceinline__ void v_read(bf16x8 (&va)[BC / 32][2][D / 32], const char* vb, const int (&voffs)[D / 32]) {
+#pragma unroll
+  for (int g = G0; g < G1; ++g)
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) {
+      const int cc = g / 2, h = g % 2;
+      const s16x4 lo = v_col4<D>(vb + voffs[mt], 32 * cc + 16 * h);
+      const s16x4 hi = v_col4<D>(vb + voffs[mt], 32 * cc + 16 * h + 8);
+      va[cc][h][mt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+}
+
 // Running softmax state of the 32 query rows of a wavefront (one row per lane pair).
 template <int D>
 struct RowState {
@@ -225,30 +245,46 @@ struct RowState {
 // round-robin, so every SIMD holds one wavefront of each group and always has
 // one of them feeding the matrix core while the other runs the softmax.
 //
-// Global step 2k:   A: softmax(k)          B: matrix(k-1)
-// Global step 2k+1: A: matrix(k)           B: loads K_{k+2}, V_{k+1}; softmax(k)
-// Group B issues every tile load during its softmax phase and waits for them
-// at the start of its next matrix phase, before its LDS transpose reads; group
-// A never has loads of its own in flight.
+// Global step 2k:   A: softmax(k)          B: loads V_{k+1}; matrix(k-1)
+// Global step 2k+1: A: matrix(k)           B: loads K_{k+2}; softmax(k)
+// Each group runs pairs (softmax(k), matrix(k)), so the PV operands and P of a
+// tile live within one pair; group B starts with a step that only loads and
+// group A ends with an empty step, which keeps their barrier counts equal.
+// The softmax phase of tile t also reads V_t's PV operands from LDS, so V_t
+// must be resident one step before its product. Group B issues every tile load
+// at the start of a step and waits for the previous step's loads at its end,
+// before the barrier; a tile issued at step s is therefore visible from step
+// s + 2, and its buffer was last read at step s - 1. Group A never has loads of
+// its own in flight.
 // ============================================================================
 
-// Barrier between phases that orders LDS only: it waits for this wavefront's
-// LDS reads and writes, not for its global->LDS loads in flight.
+// Barrier between phases. It waits for this wavefront's LDS reads and writes
+// (lgkmcnt(0)), not for its global->LDS loads in flight: a workgroup release
+// fence would also wait for those (they write LDS), which would serialise the
+// loads with the phase that issued them. The loading wavefronts instead wait
+// for their previous step's loads explicitly before this barrier. The empty asm
+// statements keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
   __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  asm volatile("" ::: "memory");
 }
 
 // VALU phase: mask (boundary tiles), tile maximum, adaptive rescale,
 // P = 2^(s*c - m) with the fp32 row sum, packed to bf16 in the PV operand order.
 template <int D, int BC, bool CAUSAL, int POLY8, bool NEG>
 __device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 32][2],
-                                              bool masked, int j0, int N, int my_q, int lane, float c, float tau) {
+                                              bf16x8 (&va)[BC / 32][2][D / 32], const char* vb,
+                                              const int (&voffs)[D / 32], bool masked, int j0, int N, int my_q,
+                                              int lane, float c, float tau) {
   constexpr int NC = BC / 32;
   constexpr int MT = D / 32;
   constexpr float mask_val = NEG ? INFINITY : -INFINITY;
   const int hl = lane >> 5;
+  // This tile's PV operands (V_t^T) are read from LDS now, so their latency
+  // hides under the exponentials; the matrix phase finds them in registers.
+  v_read<D, BC, 0, 2 * NC>(va, vb, voffs);
   if (masked) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
@@ -295,34 +331,55 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 
         st.l_sum += e;
         pb[cc][h][j] = (__bf16)e;
       }
+  // P is consumed only after the phase barrier and the row sum only at the next
+  // rescale; these empty asm uses keep both computed in this phase instead of
+  // letting them sink past the barrier (which would keep the fp32 exponentials
+  // live through the matrix phase).
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) asm volatile("" ::"v"(pb[cc][h]));
+  asm volatile("" : "+v"(st.l_sum));
 }
 
-// Matrix phase: O^T += V_t^T P_t^T (V_t in vb), then S = K_{t+1} Q^T (K_{t+1} in kb).
+// Matrix phase: O^T += V_t^T P_t^T with the V operands already in registers,
+// then S = K_{t+1} Q^T with K_{t+1} in kb. The K fragment reads are issued one
+// per PV product, so they land while the matrix core works and take the
+// registers of the V operands already consumed. After a wavefront's last tile
+// kb holds stale keys; that S is never used.
 template <int D, int BC>
 __device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 32], const bf16x8 (&pb)[BC / 32][2],
-                                             const bf16x8 (&qreg)[D / 16], const char* kb, const char* vb,
-                                             const int (&voffs)[D / 32], bool do_qk, int lane) {
+                                             const bf16x8 (&va)[BC / 32][2][D / 32], const bf16x8 (&qreg)[D / 16],
+                                             const char* kb, int lane) {
   constexpr int NC = BC / 32;
   constexpr int MT = D / 32;
+  constexpr int KK = D / 16;
+  constexpr int NPV = NC * 2 * MT;  // PV products
+  constexpr int NQK = NC * KK;      // QK products
+  static_assert(NQK == NPV, "one K fragment read per PV product");
   const int l32 = lane & 31, hl = lane >> 5;
   // Issue priority up while this wavefront feeds the matrix core, so the
   // softmax wavefront on the same SIMD does not delay its MFMA issue.
   __builtin_amdgcn_s_setprio(1);
-  const char* vrow[MT];
+  bf16x8 kf[NQK];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) vrow[mt] = vb + voffs[mt];
+  for (int i = 0; i < NPV; ++i) {
+    const int cc = i / (2 * MT), h = (i / MT) % 2, mt = i % MT;
+    st.oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][h][mt], pb[cc][h], st.oacc[mt], 0, 0, 0);
+    kf[i] = k_frag<D>(kb, 32 * (i / KK) + l32, 2 * (i % KK) + hl);
+  }
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc)
+  for (int f = 0; f < NQK; ++f) {
+    const int cc = f / KK, kk = f % KK;
+    s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[f], qreg[kk], kk == 0 ? f32x16{} : s[cc], 0, 0, 0);
+  }
+  // Instruction order: PV products each followed by one K read, then the QK products.
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const s16x4 lo = v_col4<D>(vrow[mt], 32 * cc + 16 * h);
-        const s16x4 hi = v_col4<D>(vrow[mt], 32 * cc + 16 * h + 8);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        st.oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc][h], st.oacc[mt], 0, 0, 0);
-      }
-  if (do_qk) qk_part<D, NC, 0, NC * (D / 16)>(kb, qreg, s, l32, hl);
+  for (int i = 0; i < NPV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NQK, 0);
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -374,14 +431,11 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   const int n_tiles = (kv_end + BC - 1) / BC;
   int t_full = N / BC;
   if (CAUSAL) t_full = min(t_full, (i0 + 1) / BC);
-  const int t_wave = CAUSAL ? min(n_tiles, (wq0 + 31) / BC + 1) : n_tiles;
 
-  if (grp == 1) {
-    if (n_tiles > 0) {
-      load_tile<D, BC, 4>(koff, kh, N, 0, kbuf0, wave & 3);
-      load_tile<D, BC, 4>(voff, vh, N, 0, vbuf0, wave & 3);
-    }
-    if (n_tiles > 1) load_tile<D, BC, 4>(koff, kh, N, BC, kbuf1, wave & 3);
+  if (grp == 1) {  // n_tiles >= 1
+    load_tile<D, BC, 4>(koff, kh, N, 0, kbuf0, wave & 3, true);
+    load_tile<D, BC, 4>(voff, vh, N, 0, vbuf0, wave & 3, true);
+    load_tile<D, BC, 4>(koff, kh, N, BC, kbuf1, wave & 3, n_tiles > 1);
   }
   bf16x8 qreg[KK];
   {
@@ -402,44 +456,60 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   const float tau = p.tau;
 
   f32x16 s[NC];
-  bf16x8 pb[NC][2];
-  __syncthreads();  // K_0, V_0, K_1 resident
-  if (t_wave > 0) qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, s, l32, hl);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's tile and Q loads landed
+  __syncthreads();                      // K_0, V_0, K_1 resident for every wavefront
+  qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, s, l32, hl);
 
-  // Pairs of global steps (2k, 2k+1), k = 0 .. n_tiles; kb0/vb0 hold the tiles of
-  // k's parity. The two groups run separate straight loops with the same number
-  // of barriers (two per pair).
+  // Every wavefront runs all n_tiles tiles of its workgroup: a tile past a causal
+  // row's last visible key is fully masked (P = 0) and leaves m, l and O as they
+  // are, so no wavefront takes a separate code path. Tile k's buffers are
+  // kbuf/vbuf[k % 2]. Both groups pass 2 * n_tiles + 1 barriers.
   if (grp == 0) {
     auto pair = [&](int k, char* kb1, char* vb0) {
-      if (k < t_wave) softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, k * BC, N, my_q, lane, c, tau);
+      bf16x8 pb[NC][2];
+      bf16x8 va[NC][2][MT];
+      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, va, vb0, voffs, k >= t_full, k * BC, N, my_q, lane, c, tau);
       phase_barrier();
-      if (k < t_wave) matrix_phase<D, BC>(st, s, pb, qreg, kb1, vb0, voffs, k + 1 < t_wave, lane);
+      matrix_phase<D, BC>(st, s, pb, va, qreg, kb1, lane);
       phase_barrier();
     };
     int k = 0;
-    for (; k + 1 <= n_tiles; k += 2) {
+    for (; k + 1 < n_tiles; k += 2) {
       pair(k, kbuf1, vbuf0);
       pair(k + 1, kbuf0, vbuf1);
     }
-    if (k <= n_tiles) pair(k, kbuf1, vbuf0);
+    if (k < n_tiles) pair(k, kbuf1, vbuf0);
+    phase_barrier();
   } else {
-    auto pair = [&](int k, char* kb0, char* vb1) {
-      if (k >= 1 && k - 1 < t_wave) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // own loads landed before the transpose reads (vmcnt(0))
-        matrix_phase<D, BC>(st, s, pb, qreg, kb0, vb1, voffs, k < t_wave, lane);
-      }
+    // Every step issues LPW loads per wavefront; waiting until only the newest LPW
+    // are outstanding (vmcnt counts this wavefront's loads in issue order) means
+    // the previous step's loads have landed.
+    auto wait_prev = [] { __builtin_amdgcn_s_waitcnt(0x0F70 | LPW); };  // vmcnt(LPW)
+    // Step 0: V_1 in flight.
+    load_tile<D, BC, 4>(voff, vh, N, BC, vbuf1, wave & 3, n_tiles > 1);
+    wait_prev();
+    phase_barrier();
+    // Steps 2k+1 (loads K_{k+2}; softmax(k)) and 2k+2 (loads V_{k+2}; matrix(k)).
+    auto pair = [&](int k, char* kb0, char* kb1, char* vb0) {
+      bf16x8 pb[NC][2];
+      bf16x8 va[NC][2][MT];
+      const bool live = k + 2 < n_tiles;
+      load_tile<D, BC, 4>(koff, kh, N, (k + 2) * BC, kb0, wave & 3, live);
+      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, va, vb0, voffs, k >= t_full, k * BC, N, my_q, lane, c, tau);
+      wait_prev();
       phase_barrier();
-      if (k + 2 < n_tiles) load_tile<D, BC, 4>(koff, kh, N, (k + 2) * BC, kb0, wave & 3);
-      if (k + 1 < n_tiles) load_tile<D, BC, 4>(voff, vh, N, (k + 1) * BC, vb1, wave & 3);
-      if (k < t_wave) softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, k * BC, N, my_q, lane, c, tau);
+      load_tile<D, BC, 4>(voff, vh, N, (k + 2) * BC, vb0, wave & 3, live);
+      matrix_phase<D, BC>(st, s, pb, va, qreg, kb1, lane);
+      wait_prev();
       phase_barrier();
     };
     int k = 0;
-    for (; k + 1 <= n_tiles; k += 2) {
-      pair(k, kbuf0, vbuf1);
-      pair(k + 1, kbuf1, vbuf0);
+    for (; k + 1 < n_tiles; k += 2) {
+      pair(k, kbuf0, kbuf1, vbuf0);
+      pair(k + 1, kbuf1, kbuf0, vbuf1);
     }
-    if (k <= n_tiles) pair(k, kbuf0, vbuf1);
+    if (k < n_tiles) pair(k, kbuf0, kbuf1, vbuf0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
   }
 
   const float l_tot = pair_sum(st.l_sum);
