@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+
+#include <atomic>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -41,11 +43,32 @@ template <int D> struct Cfg;
 template <> struct Cfg<128> { static constexpr int BC = 64; };
 template <> struct Cfg<64> { static constexpr int BC = 64; };
 
+// Compute units per XCD of the current device (8 XCDs per MI355X), cached per
+// device; 0 if the runtime cannot tell (then every tile gets its own workgroup).
+int cus_per_xcd() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) return 0;
+    v = cus / 8;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 template <int D, bool CAUSAL, bool OF32, int POLY8>
 hipError_t launch(const attn::Params& p, bool neg, hipStream_t stream) {
   // hipLaunchKernel reports this launch's own error (no sticky state from other calls).
   // A negative scale flips the row maximum of s*c into c * min(s): separate instantiation.
-  const dim3 grid(p.per_xcd * 8), block(64 * kWaves);
+  // One workgroup per compute unit walks its XCD's tile range, so the next tile's
+  // loads overlap the current tile's epilogue (causal: in a length-balanced order).
+  int per_wg_xcd = p.per_xcd;
+  const int slots = cus_per_xcd();
+  if (slots > 0 && slots < per_wg_xcd) per_wg_xcd = slots;
+  const dim3 grid(per_wg_xcd * 8), block(64 * kWaves);
   void* args[] = {const_cast<attn::Params*>(&p)};
   const void* fn = neg ? reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, OF32, POLY8, true>)
                        : reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, OF32, POLY8, false>);

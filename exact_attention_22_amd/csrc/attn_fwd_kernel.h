@@ -111,43 +111,51 @@ __device__ __forceinline__ int vswz(int r) {
   return D == 128 ? (4 * (r & 3)) : (4 * ((r >> 1) & 1));
 }
 
-// Loads of one BC-row tile of K or V into an LDS tile buffer. Wave w fills the
-// 1 KiB wave-loads w*LPW .. w*LPW+LPW-1; load_offsets gives each lane's byte
-// offset within a tile (fixed for the whole kernel), and the buffer resource is
-// rebased on the tile's first row in scalar registers, so rows past N read as
-// zeros and no per-tile vector arithmetic is needed. (Free functions: a device
-// member function calling these builtins breaks the kernel's host-side stub.)
+// Loads of one BC-row tile of K or V into an LDS tile buffer by NW wavefronts.
+// Each wave instruction fills 1 KiB (RPL consecutive rows); wave-load i of
+// wavefront w covers rows RPL*(NW*i + w) .. +RPL-1. With that assignment the
+// row's swizzle does not depend on i, so one per-lane byte offset (load_offset,
+// fixed for the whole kernel) serves every load of a wavefront: load i reads
+// from a buffer resource rebased by i*RPL*NW rows in scalar registers. The
+// resources end at row N, so rows past N read as zeros with no per-tile vector
+// arithmetic. (Free functions: a device member function calling these builtins
+// breaks the kernel's host-side stub.)
 template <int D, int BC, int NW>
 struct LoadShape {
   static constexpr int CH = D / 8;            // 16-byte chunks per row
   static constexpr int RPL = 64 / CH;         // rows per wave-load
   static constexpr int LPW = BC / RPL / NW;   // wave-loads per wave
+  static constexpr int STEP = RPL * NW * D * 2;  // bytes between a wavefront's loads
   static_assert(BC % (RPL * NW) == 0, "load split");
 };
 
 template <int D, int BC, int NW, bool ISK>
-__device__ __forceinline__ void load_offsets(uint32_t* off, int wave, int lane) {
+__device__ __forceinline__ uint32_t load_offset(int wave, int lane) {
   using S = LoadShape<D, BC, NW>;
-#pragma unroll
-  for (int i = 0; i < S::LPW; ++i) {
-    const int r = (wave * S::LPW + i) * S::RPL + lane / S::CH;
-    const int c = (lane % S::CH) ^ (ISK ? kswz<D>(r) : vswz<D>(r));
-    off[i] = (uint32_t)(r * D + 8 * c) * 2;
-  }
+  const int r = wave * S::RPL + lane / S::CH;  // row of load 0; load i adds RPL*NW*i rows
+  const int c = (lane % S::CH) ^ (ISK ? kswz<D>(r) : vswz<D>(r));
+  return (uint32_t)(r * D + 8 * c) * 2;
 }
 
-// A tile that is not `live` (past the last tile) gets a zero-size resource: its
+// A tile that is not `live` (past the last tile) gets zero-size resources: its
 // loads fill the buffer with zeros without touching memory, so every step issues
 // the same loads and the load/wait sequence has no branches.
 template <int D, int BC, int NW>
-__device__ __forceinline__ void load_tile(const uint32_t* off, const __bf16* head, int N, int j0, char* buf,
-                                          int wave, bool live) {
+__device__ __forceinline__ void load_tile(uint32_t off, const __bf16* head, int N, int j0, char* buf, int wave,
+                                          bool live) {
   using S = LoadShape<D, BC, NW>;
-  const __amdgpu_buffer_rsrc_t rsrc =
-      buffer_rsrc(head + (size_t)(live ? j0 : 0) * D, live ? (uint32_t)(N - j0) * D * 2 : 0u);
+  const char* base = (const char*)(head + (size_t)(live ? j0 : 0) * D);
+  const uint32_t bytes = live ? (uint32_t)(N - j0) * D * 2 : 0u;
 #pragma unroll
-  for (int i = 0; i < S::LPW; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(buf + (wave * S::LPW + i) * 1024), 16, off[i], 0, 0, 0);
+  for (int i = 0; i < S::LPW; ++i) {
+    const uint32_t skip = (uint32_t)(i * S::STEP);
+    // readfirstlane keeps the (uniform) record count in a scalar register: the
+    // compiler computes the clamped difference on the VALU, and a resource in
+    // vector registers would need a loop over lanes.
+    const uint32_t rec = __builtin_amdgcn_readfirstlane(bytes > skip ? bytes - skip : 0u);
+    const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(base + skip, rec);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(buf + (NW * i + wave) * 1024), 16, off, 0, 0, 0);
+  }
 }
 
 // K fragment (A operand of S^T = K Q^T): row R, 16-byte chunk c.
@@ -398,53 +406,88 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   __shared__ __attribute__((aligned(1024))) char vbuf0[TILEB];
   __shared__ __attribute__((aligned(1024))) char vbuf1[TILEB];
 
-  const int wg = blockIdx.x;
-  const int logical = (wg & 7) * p.per_xcd + (wg >> 3);
-  if (logical >= p.total_tiles) return;
-  const int bh = logical / p.nq_tiles;
-  int qt = logical - bh * p.nq_tiles;
-  if (CAUSAL) qt = p.nq_tiles - 1 - qt;  // longest rows first
-  const int N = p.N;
-  const int i0 = qt * BR;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;  // 0: group A, 1: group B
   const int l32 = lane & 31;
   const int hl = lane >> 5;
-  const int wq0 = i0 + wave * 32;
-  const int my_q = wq0 + l32;
-
-  const __bf16* const kh = p.k + head;
-  const __bf16* const vh = p.v + head;
+  const int N = p.N;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
   constexpr int LPW = LoadShape<D, BC, 4>::LPW;  // group B's four wavefronts load every tile
-  uint32_t koff[LPW], voff[LPW];
-  load_offsets<D, BC, 4, true>(koff, wave & 3, lane);
-  load_offsets<D, BC, 4, false>(voff, wave & 3, lane);
+  const uint32_t koff = load_offset<D, BC, 4, true>(wave & 3, lane);
+  const uint32_t voff = load_offset<D, BC, 4, false>(wave & 3, lane);
   int voffs[MT];
   v_offsets<D>(voffs, lane);
+  const float c = p.c;
+  const float tau = p.tau;
 
-  const int kv_end = CAUSAL ? min(N, i0 + BR) : N;
-  const int n_tiles = (kv_end + BC - 1) / BC;
-  int t_full = N / BC;
-  if (CAUSAL) t_full = min(t_full, (i0 + 1) / BC);
-
-  if (grp == 1) {  // n_tiles >= 1
-    load_tile<D, BC, 4>(koff, kh, N, 0, kbuf0, wave & 3, true);
-    load_tile<D, BC, 4>(voff, vh, N, 0, vbuf0, wave & 3, true);
-    load_tile<D, BC, 4>(koff, kh, N, BC, kbuf1, wave & 3, n_tiles > 1);
-  }
+  // Tile v of the launch's virtual sequence: workgroup slot v runs logical tile
+  // (v % 8) * per_xcd + v / 8, so each XCD (slots are dealt round-robin to the 8
+  // XCDs) works through a contiguous range of tiles and the query tiles of one
+  // head share that XCD's L2. A launch with fewer workgroups than slots walks
+  // the slots v, v + gridDim.x, ... (gridDim.x is a multiple of 8, so a
+  // workgroup stays on its XCD's range); the next tile's Q, K_0, V_0 and K_1
+  // loads are then issued before the current tile's epilogue.
+  struct Tile {
+    int bh, i0, n_tiles, t_full;
+  };
+  // Causal: a persistent workgroup's successive tiles alternate direction
+  // through its XCD's range (round r of S slots takes position i or S-1-i). The
+  // range is ordered head by head with the longest query tiles first, so this
+  // pairs long tiles with short ones and every workgroup gets about the same
+  // work, while the tiles running at the same time stay within few heads (their
+  // K and V share the XCD's L2).
+  const int S = (int)gridDim.x >> 3;  // workgroups per XCD
+  auto tile_of = [&](int v, Tile& t) -> bool {
+    int j = v >> 3;
+    if (CAUSAL) {
+      const int r = j / S, i = j - r * S;
+      j = r * S + ((r & 1) ? S - 1 - i : i);
+    }
+    const int logical = (v & 7) * p.per_xcd + j;
+    if (j >= p.per_xcd || logical >= p.total_tiles) return false;
+    t.bh = logical / p.nq_tiles;
+    int qt = logical - t.bh * p.nq_tiles;
+    if (CAUSAL) qt = p.nq_tiles - 1 - qt;  // longest rows first
+    t.i0 = qt * BR;
+    const int kv_end = CAUSAL ? min(N, t.i0 + BR) : N;
+    t.n_tiles = (kv_end + BC - 1) / BC;
+    t.t_full = N / BC;
+    if (CAUSAL) t.t_full = min(t.t_full, (t.i0 + 1) / BC);
+    return true;
+  };
   bf16x8 qreg[KK];
-  {
+  auto issue_loads = [&](const Tile& t) {
+    const size_t head = (size_t)t.bh * (size_t)N * D;
+    if (grp == 1) {  // n_tiles >= 1
+      load_tile<D, BC, 4>(koff, p.k + head, N, 0, kbuf0, wave & 3, true);
+      load_tile<D, BC, 4>(voff, p.v + head, N, 0, vbuf0, wave & 3, true);
+      load_tile<D, BC, 4>(koff, p.k + head, N, BC, kbuf1, wave & 3, t.n_tiles > 1);
+    }
     const __amdgpu_buffer_rsrc_t qrsrc = buffer_rsrc(p.q + head, head_bytes);
+    const int q_row = t.i0 + wave * 32 + l32;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       qreg[kk] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (uint32_t)(my_q * D + 16 * kk + 8 * hl) * 2, 0, 0));
-  }
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (uint32_t)(q_row * D + 16 * kk + 8 * hl) * 2, 0, 0));
+  };
+
+  int slot = blockIdx.x;
+  Tile tile;
+  if (!tile_of(slot, tile)) return;
+  issue_loads(tile);
+  for (;;) {
+  const int bh = tile.bh;
+  const int i0 = tile.i0;
+  const int n_tiles = tile.n_tiles;
+  const int t_full = tile.t_full;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const int wq0 = i0 + wave * 32;
+  const int my_q = wq0 + l32;
+  const __bf16* const kh = p.k + head;
+  const __bf16* const vh = p.v + head;
+
   RowState<D> st;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) st.oacc[mt] = f32x16{};
@@ -452,8 +495,6 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   st.thr = -INFINITY;
   st.l_sum = 0.f;
   st.n_rescale = 0;
-  const float c = p.c;
-  const float tau = p.tau;
 
   f32x16 s[NC];
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's tile and Q loads landed
@@ -509,8 +550,14 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
       pair(k + 1, kbuf1, kbuf0, vbuf1);
     }
     if (k < n_tiles) pair(k, kbuf0, kbuf1, vbuf0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
   }
+
+  // Every wavefront has passed the last barrier, so no LDS tile and no Q
+  // register is read again: the next tile's loads can go out now and land
+  // while this tile's output is written.
+  Tile next;
+  const bool more = tile_of(slot + (int)gridDim.x, next);
+  if (more) issue_loads(next);
 
   const float l_tot = pair_sum(st.l_sum);
   if (my_q < N) {
@@ -538,6 +585,11 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
       if (p.rescale_count) p.rescale_count[row] = st.n_rescale;
     }
   }
+  if (!more) break;
+  tile = next;
+  slot += (int)gridDim.x;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
 }
 
 }  // namespace attn

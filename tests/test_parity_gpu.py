@@ -42,6 +42,34 @@ def test_workload_sampled(name):
     check_sampled(q, k, v, w.causal, w.scale, o, lse, picks, name)
 
 
+# ---------------------------------------------------------------- persistent tile walk
+# A launch has at most one workgroup per compute unit; each walks the query tiles
+# of its XCD's range (causal: alternating direction every round). These shapes
+# give several rounds per workgroup, a partial last round (even and odd, i.e.
+# forward and reversed) and a partial last XCD range. O and LSE start as NaN, so a
+# tile that no workgroup writes shows up as non-finite output.
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (2, 50, 2048, 64, True),     # 800 tiles, 100 per XCD: odd (reversed) partial last round
+    (1, 101, 1792, 64, True),    # 707 tiles, 89 per XCD, last XCD range 84: even partial rounds
+    (1, 101, 1792, 128, False),  # the same walk without the reversal
+    (3, 7, 4096, 128, True),     # 336 tiles, 42 per XCD
+])
+def test_persistent_walk_shapes(B, H, N, d, causal):
+    note(f"persistent walk: B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = inputs.draw(B, H, N, d, seed=B * 1000 + H + N + d + causal)
+    scale = 1.0 / math.sqrt(d)
+    dev = device()
+    o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=dev)
+    binding.attention(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_h = o.float().cpu().numpy().astype(np.float64)
+    l_h = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o_h)) and np.all(np.isfinite(l_h)), "some query tile was not written"
+    picks = sample_picks(B, H, N, seed=N + H, full_heads=((B - 1, H - 1),))
+    check_sampled(q, k, v, causal, scale, o_h, l_h, picks, f"B={B} H={H} N={N} d={d} causal={causal}")
+
+
 # ---------------------------------------------------------------- ragged / small shapes
 SWEEP_N = [1, 2, 7, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000]
 
