@@ -14,6 +14,8 @@ Workloads (B heads-batch, H heads, N tokens, d head dim), all i.i.d. N(0,1):
   drift8k   2 x 16 x  8192 x  64  causal, with a per-key logit drift: key j
             gets 0.002*j*u and every query gets u, u = ones(d)/sqrt(d), so the
             running row maximum keeps rising along the keys.
+  gqa8k     2 x 32 x  8192 x 128  causal, grouped-query: 8 key/value heads,
+            each shared by 4 consecutive query heads (k, v are [2, 8, 8192, 128]).
 """
 from __future__ import annotations
 
@@ -34,6 +36,11 @@ class Workload:
     causal: bool
     drift: bool
     seed: int
+    Hkv: int = 0  # key/value heads; 0 means H (ordinary multi-head attention)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:
@@ -53,6 +60,7 @@ WORKLOADS = [
     Workload("headline", 2, 32, 8192, 128, False, False, 1003),
     Workload("long32k", 1, 32, 32768, 128, True, False, 1004),
     Workload("drift8k", 2, 16, 8192, 64, True, True, 1005),
+    Workload("gqa8k", 2, 32, 8192, 128, True, False, 1006, Hkv=8),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -60,10 +68,19 @@ BY_NAME = {w.name: w for w in WORKLOADS}
 def draw(B: int, H: int, N: int, d: int, seed: int, drift: bool = False,
          drift_rate: float = 0.002):
     """Draw (q, k, v) as bfloat16 CPU tensors [B,H,N,d], in that order, from one seed."""
+    return draw_gqa(B, H, H, N, d, seed, drift, drift_rate)
+
+
+def draw_gqa(B: int, H: int, Hkv: int, N: int, d: int, seed: int, drift: bool = False,
+             drift_rate: float = 0.002):
+    """Draw q [B,H,N,d] and k, v [B,Hkv,N,d] as bfloat16 CPU tensors, in that order.
+
+    With Hkv = H this is exactly `draw`.
+    """
     g = torch.Generator(device="cpu").manual_seed(seed)
     q = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
-    k = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
-    v = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
     if drift:
         u = torch.full((d,), 1.0 / math.sqrt(d), dtype=torch.float32)
         j = torch.arange(N, dtype=torch.float32).view(1, 1, N, 1)
@@ -74,7 +91,7 @@ def draw(B: int, H: int, N: int, d: int, seed: int, drift: bool = False,
 
 def workload_inputs(w: Workload, seed: int | None = None):
     """Inputs of a named workload (its own seed unless one is given)."""
-    return draw(w.B, w.H, w.N, w.d, w.seed if seed is None else seed, w.drift)
+    return draw_gqa(w.B, w.H, w.kv_heads, w.N, w.d, w.seed if seed is None else seed, w.drift)
 
 
 def digest(*tensors) -> str:

@@ -10,4 +10,8 @@ from .exact import (  # noqa: F401
     attention_probs,
     tiled_online_attention,
     brute_force_attention,
+    attention_gqa,
+    attention_gqa_rows,
+    brute_force_attention_gqa,
+    kv_head,
 )

@@ -24,6 +24,14 @@ J(i) = all keys (non-causal) or keys j <= i (causal, lower-triangular mask).
 Inputs are widened exactly to float64 (bfloat16 and float32 values are exact
 in float64), and `scale` is the float32 value the kernel uses, widened.
 
+Grouped-query attention (`attention_gqa`): several query heads share one key and
+value head ([LK] "Key points" and "Compatibility and current status", which name
+GQA/MQA among the configurations earlier FlashAttention versions supported).
+The pages do not say which query heads share a key/value head; the reading used
+here is consecutive groups: with H query heads and Hkv key/value heads (Hkv
+divides H), query head h reads key/value head floor(h / (H / Hkv)). MQA is
+Hkv = 1; Hkv = H is ordinary multi-head attention.
+
 `tiled_online_attention` is a second, test-only float64 model that follows the
 algorithm the pages describe: tiles of queries and keys, a running maximum and
 running sum per query row ([JG] "Online softmax and recomputation";
@@ -93,6 +101,53 @@ def attention(q, k, v, causal: bool, scale: float, row_block: int = 1024):
     return o, lse
 
 
+def _check_gqa_shapes(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape:
+        raise ValueError(f"expected q [B,H,N,d] and k, v [B,Hkv,N,d], got {q.shape} {k.shape} {v.shape}")
+    B, H, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or k.shape[1] < 1 or H % k.shape[1]:
+        raise ValueError(f"key/value heads {k.shape[1]} must divide query heads {H}; shapes {q.shape} {k.shape}")
+
+
+def kv_head(h: int, H: int, Hkv: int) -> int:
+    """Key/value head read by query head h (consecutive groups of H / Hkv query heads)."""
+    return h // (H // Hkv)
+
+
+def attention_gqa(q, k, v, causal: bool, scale: float, row_block: int = 1024):
+    """Exact grouped-query attention forward, float64. q: [B,H,N,d]; k, v: [B,Hkv,N,d].
+
+    Each query head is the definition above evaluated against its key/value head.
+    Returns (O[B,H,N,d], LSE[B,H,N]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    _check_gqa_shapes(q, k, v)
+    scale = float(np.float64(scale))
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    o = np.empty((B, H, N, d))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, Hkv)
+            for r0 in range(0, N, row_block):
+                rows = np.arange(r0, min(N, r0 + row_block))
+                o[b, h, rows], lse[b, h, rows] = _rows_of_head(q[b, h], k[b, g], v[b, g], rows, causal, scale)
+    return o, lse
+
+
+def attention_gqa_rows(q, k, v, causal: bool, scale: float, picks):
+    """`attention_gqa` evaluated only at sampled outputs (picks as in `attention_rows`)."""
+    scale = float(np.float64(scale))
+    H, Hkv = q.shape[1], k.shape[1]
+    out = []
+    for b, h, rows in picks:
+        g = kv_head(h, H, Hkv)
+        qh, kh, vh = _f64(q[b, h]), _f64(k[b, g]), _f64(v[b, g])
+        out.append(_rows_of_head(qh, kh, vh, np.asarray(rows, dtype=np.int64), causal, scale))
+    return out
+
+
 def attention_rows(q, k, v, causal: bool, scale: float, picks):
     """Definition evaluated only at sampled outputs.
 
@@ -147,6 +202,30 @@ def brute_force_attention(q, k, v, causal: bool, scale: float):
                 for c in range(d):
                     o[b][h][i][c] = sum(wj * v[b][h][j][c] for wj, j in zip(w, keys)) / z
                 lse[b][h][i] = math.log(z)
+    return np.array(o), np.array(lse)
+
+
+def brute_force_attention_gqa(q, k, v, causal: bool, scale: float):
+    """Pure-Python loops for grouped-query attention (tiny inputs only), without the
+    max shift. The head map is walked from the key/value side: key/value head g
+    serves the query heads g*G .. g*G + G - 1, G = H / Hkv."""
+    q, k, v = (_f64(t).tolist() for t in (q, k, v))
+    scale = float(np.float64(scale))
+    B, H, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Hkv = len(k[0])
+    G = H // Hkv
+    o = [[[[0.0] * d for _ in range(N)] for _ in range(H)] for _ in range(B)]
+    lse = [[[0.0] * N for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for g in range(Hkv):
+            for h in range(g * G, g * G + G):
+                for i in range(N):
+                    keys = range(i + 1) if causal else range(N)
+                    w = [math.exp(scale * sum(q[b][h][i][c] * k[b][g][j][c] for c in range(d))) for j in keys]
+                    z = sum(w)
+                    for c in range(d):
+                        o[b][h][i][c] = sum(wj * v[b][g][j][c] for wj, j in zip(w, keys)) / z
+                    lse[b][h][i] = math.log(z)
     return np.array(o), np.array(lse)
 
 

@@ -10,7 +10,8 @@ def test_workloads_as_stated():
     shapes = [(w.B, w.H, w.N, w.d, w.causal, w.drift) for w in inputs.WORKLOADS]
     assert shapes == [(1, 2, 256, 64, False, False), (4, 16, 2048, 128, True, False),
                       (2, 32, 8192, 128, False, False), (1, 32, 32768, 128, True, False),
-                      (2, 16, 8192, 64, True, True)]
+                      (2, 16, 8192, 64, True, True), (2, 32, 8192, 128, True, False)]
+    assert [w.kv_heads for w in inputs.WORKLOADS] == [2, 16, 32, 32, 16, 8]
     for w in inputs.WORKLOADS:
         assert w.scale == torch.tensor(1 / math.sqrt(w.d), dtype=torch.float32).item()
     assert inputs.BY_NAME["headline"].flops == 4.0 * 2 * 32 * 8192 ** 2 * 128
@@ -48,3 +49,11 @@ def test_value_magnitude_budget():
     """|V| stays under 8 so one bf16 half-ulp of O stays under the 2e-2 budget."""
     _, _, v = inputs.draw(2, 16, 8192, 64, seed=1005)
     assert v.float().abs().max().item() < 8.0
+
+
+def test_gqa_draw_shapes_and_mha_case():
+    q, k, v = inputs.draw_gqa(2, 8, 2, 16, 4, seed=11)
+    assert q.shape == (2, 8, 16, 4) and k.shape == v.shape == (2, 2, 16, 4)
+    a = inputs.draw_gqa(1, 3, 3, 16, 4, seed=12)
+    b = inputs.draw(1, 3, 16, 4, seed=12)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
