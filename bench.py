@@ -34,8 +34,8 @@ KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip", "exp2_poly.h")
 # counter reads for a 256 MiB device copy (FETCH x2.0, WRITE x1.0); see
 # profiles/attn_fwd_headline_counters.md. Valid only for the kernel sources
 # with this SHA-256; any change to them reports traffic as null.
-TRAFFIC = {"sources_sha256": "e44aa2948cd8782ce5ab45b44e6be56c08dd15f71de77114d1f08af4d7426587",
-           "fetch_kib": 215000.0, "write_kib": 140800.0, "fetch_scale": 2.0, "write_scale": 1.0}
+TRAFFIC = {"sources_sha256": "e93797d23a89be5ae574f5e8ae0caba1f1b5ab7c2413b1313b9f62eb0784d670",
+           "fetch_kib": 214600.0, "write_kib": 140800.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def kernel_sources_sha256() -> str:
@@ -59,7 +59,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--no-others", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-others", action="store_true",
+                    help="time only the K headline steps (no other workloads, no sampled timing)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle time")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (calibrates profiler byte counters)")
@@ -93,6 +94,48 @@ def time_workload(w, steps, warmup, **kw):
     return ms
 
 
+def time_samples(w, n_samples=20, min_ms=50.0):
+    """n_samples timed batches of back-to-back launches, each at least min_ms long;
+    per-launch median and min (ms)."""
+    import torch
+
+    from exact_attention_22_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inputs.workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def batch(n):
+        start.record(stream)
+        for _ in range(n):
+            binding.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    one = batch(3) / 3
+    per_batch = max(1, int(math.ceil(min_ms / max(one, 1e-3))))
+    ms = sorted(batch(per_batch) / per_batch for _ in range(n_samples))
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return {"n": n_samples, "launches_each": per_batch, "median_ms": round(ms[len(ms) // 2], 4),
+            "min_ms": round(ms[0], 4)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, target_s):
     """Time the fp64 oracle (as it stands) on a bounded sample: whole heads of the
     workload, as many as fit the target time; returned in TFLOP/s of the metric."""
@@ -117,7 +160,8 @@ def cpu_baseline(w, target_s):
     flops = w.flops / (w.B * w.H) * heads
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} heads of {w.name} (full rows), {dt:.1f} s fp64 numpy",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "cpu_model": cpu_model(),
+            "full_workload_seconds_extrapolated": round(dt * w.B * w.H / heads, 1)}
 
 
 def main():
@@ -141,6 +185,11 @@ def main():
     ms = time_workload(w, args.steps, args.warmup)
     wall = time.perf_counter() - t0
     tflops = w.flops / (ms * 1e-3) / 1e12
+    samples = None
+    if not args.no_others:  # 20 batches of >= 50 ms of back-to-back launches: median and min
+        samples = time_samples(w)
+        samples["median_tflops"] = round(w.flops / (samples["median_ms"] * 1e-3) / 1e12, 1)
+        samples["max_tflops"] = round(w.flops / (samples["min_ms"] * 1e-3) / 1e12, 1)
 
     if args.copy_mib:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda:0")
@@ -158,7 +207,7 @@ def main():
             ot = o.flops / (oms * 1e-3) / 1e12
             others[o.name] = {"ms": round(oms, 4), "tflops": round(ot, 1),
                               "frac_peak": round(ot / PEAK_BF16_TFLOPS, 4), "causal": o.causal,
-                              "shape": [o.B, o.H, o.N, o.d]}
+                              "shape": [o.B, o.H, o.N, o.d], "kv_heads": o.kv_heads}
 
     line = {
         "metric": "attention fwd TFLOP/s (bf16, causal & non-causal) and % of MI355X MFMA peak",
@@ -173,18 +222,20 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} "
-                               f"bf16 N(0,1) seed {w.seed}",
-                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal},
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} Hkv={w.kv_heads} N={w.N} d={w.d} "
+                               f"causal={w.causal} bf16 N(0,1) seed {w.seed}",
+                   "B": w.B, "H": w.H, "Hkv": w.kv_heads, "N": w.N, "d": w.d, "causal": w.causal},
         "frac_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(w.name)},
         "timed_wall_s": round(wall, 2),
+        "samples": samples,
         "workloads": others,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["gpu_speedup_vs_cpu_baseline"] = round(tflops / line["cpu_baseline"]["value"], 1)
     print(json.dumps(line), flush=True)
 
 

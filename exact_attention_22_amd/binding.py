@@ -22,7 +22,9 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_DIM", 3: "ATTN_ERR_UNSU
           8: "ATTN_ERR_OPTS"}
 O_BF16, O_F32 = 0, 1
 EXPORTS = ["attn_fwd", "attn_fwd_ex", "attn_fwd_check", "attn_fwd_opts_init", "attn_status_str",
-           "attn_last_error", "attn_abi_version", "attn_exp2_poly_host", "attn_fwd_tile_shape"]
+           "attn_last_error", "attn_abi_version", "attn_exp2_poly_host", "attn_fwd_tile_shape",
+           "attn_fwd_gqa", "attn_fwd_gqa_check"]
+ABI_VERSION = 2
 
 
 class AttnFwdOpts(ctypes.Structure):
@@ -55,6 +57,11 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_ex.restype = i
         L.attn_fwd_check.argtypes = tensor_args + [ctypes.POINTER(AttnFwdOpts)]
         L.attn_fwd_check.restype = i
+        gqa_args = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, ctypes.POINTER(AttnFwdOpts)]
+        L.attn_fwd_gqa.argtypes = gqa_args + [vp]
+        L.attn_fwd_gqa.restype = i
+        L.attn_fwd_gqa_check.argtypes = gqa_args
+        L.attn_fwd_gqa_check.restype = i
         L.attn_fwd_opts_init.argtypes = [ctypes.POINTER(AttnFwdOpts)]
         L.attn_fwd_opts_init.restype = None
         L.attn_status_str.argtypes = [i]
@@ -111,6 +118,17 @@ def attn_fwd_check(q, k, v, o, lse, B, H, N, d, causal, scale, opts: AttnFwdOpts
                                 ctypes.byref(opts) if opts is not None else None)
 
 
+def attn_fwd_gqa(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Hkv: int, N: int, d: int,
+                 causal: int, scale: float, opts: AttnFwdOpts | None, stream: int | None) -> int:
+    return lib().attn_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, d, int(causal), scale,
+                              ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def attn_fwd_gqa_check(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, opts: AttnFwdOpts | None = None) -> int:
+    return lib().attn_fwd_gqa_check(q, k, v, o, lse, B, H, Hkv, N, d, int(causal), scale,
+                                    ctypes.byref(opts) if opts is not None else None)
+
+
 def _check_tensor(name, t, shape=None):
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
@@ -128,14 +146,18 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
               lse: torch.Tensor | None = None, rescale_count: bool = False):
     """Exact attention forward on the current stream: returns (O, LSE[, rescale counts]).
 
-    q, k, v: bfloat16 [B,H,N,d] contiguous device tensors; scale defaults to 1/sqrt(d)
-    (as a float32). O has `out_dtype` (bfloat16 or float32); LSE is float32 [B,H,N].
+    q: bfloat16 [B,H,N,d]; k, v: bfloat16 [B,Hkv,N,d] with Hkv dividing H (Hkv < H is
+    grouped-query attention: query head h reads key/value head h // (H // Hkv)); all
+    contiguous device tensors. scale defaults to 1/sqrt(d) (as a float32). O has
+    `out_dtype` (bfloat16 or float32); LSE is float32 [B,H,N].
     """
     _check_tensor("q", q)
     shape = tuple(q.shape)
-    _check_tensor("k", k, shape)
-    _check_tensor("v", v, shape)
     B, H, N, d = shape
+    _check_tensor("k", k)
+    Hkv = k.shape[1]
+    _check_tensor("k", k, (B, Hkv, N, d))
+    _check_tensor("v", v, (B, Hkv, N, d))
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
     if out_dtype not in (torch.bfloat16, torch.float32):
@@ -148,8 +170,12 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     opts = make_opts(tau, poly_eighths, O_F32 if out_dtype == torch.float32 else O_BF16,
                      counts.data_ptr() if counts is not None else None)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                     B, H, N, d, causal, scale, opts, stream)
+    if Hkv == H:
+        st = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         B, H, N, d, causal, scale, opts, stream)
+    else:
+        st = attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, Hkv, N, d, causal, scale, opts, stream)
     if st != ATTN_OK:
         raise AttnError(st, last_error())
     return (out, lse, counts) if rescale_count else (out, lse)

@@ -91,24 +91,8 @@ hipError_t launch_d(const attn::Params& p, bool causal, bool of32, int poly8, bo
   return of32 ? launch_poly<D, false, true>(p, poly8, neg, s) : launch_poly<D, false, false>(p, poly8, neg, s);
 }
 
-}  // namespace
-
-extern "C" {
-
-void attn_fwd_opts_init(attn_fwd_opts* opts) {
-  if (!opts) return;
-  memset(opts, 0, sizeof *opts);
-  opts->struct_size = sizeof *opts;
-  opts->rescale_tau_log2 = 8.0f;
-  opts->exp2_poly_eighths = 0;
-  opts->o_dtype = ATTN_O_BF16;
-  opts->rescale_count = nullptr;
-}
-
-attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const void* o,
-                             const float* lse, int B, int H, int N, int d, int causal,
-                             float scale, const attn_fwd_opts* opts) {
-  (void)causal;
+attn_status_t check_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+                         int H, int Hkv, int N, int d, float scale, const attn_fwd_opts* opts) {
   g_last_error[0] = '\0';
   attn_fwd_opts def;
   attn_fwd_opts_init(&def);
@@ -118,6 +102,8 @@ attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const 
     def = *opts;
   }
   if (B < 0 || H < 0 || N < 0) return fail(ATTN_ERR_DIM, "negative size B=%d H=%d N=%d", B, H, N);
+  if (H > 0 ? (Hkv < 1 || Hkv > H || H % Hkv != 0) : Hkv != 0)
+    return fail(ATTN_ERR_DIM, "key/value heads Hkv=%d must divide query heads H=%d", Hkv, H);
   if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
   if (!isfinite(scale)) return fail(ATTN_ERR_SCALE, "scale is not finite");
   if (!(def.rescale_tau_log2 >= 0.f && def.rescale_tau_log2 <= 64.f))
@@ -141,14 +127,16 @@ attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const 
   if (def.rescale_count && ((uintptr_t)def.rescale_count & 3))
     return fail(ATTN_ERR_MISALIGNED, "rescale_count must be 4-byte aligned");
 
-  const size_t in_bytes = (size_t)rows * d * 2;
+  const size_t q_bytes = (size_t)rows * d * 2;
+  const size_t kv_bytes = (size_t)B * Hkv * N * d * 2;
   const size_t o_bytes = (size_t)rows * d * (def.o_dtype == ATTN_O_F32 ? 4 : 2);
   const size_t l_bytes = (size_t)rows * 4;
   const void* ins[3] = {q, k, v};
-  for (const void* in : ins) {
-    if (overlaps(o, o_bytes, in, in_bytes)) return fail(ATTN_ERR_ALIAS, "o overlaps an input");
-    if (overlaps(lse, l_bytes, in, in_bytes)) return fail(ATTN_ERR_ALIAS, "lse overlaps an input");
-    if (def.rescale_count && overlaps(def.rescale_count, l_bytes, in, in_bytes))
+  const size_t in_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(o, o_bytes, ins[i], in_bytes[i])) return fail(ATTN_ERR_ALIAS, "o overlaps an input");
+    if (overlaps(lse, l_bytes, ins[i], in_bytes[i])) return fail(ATTN_ERR_ALIAS, "lse overlaps an input");
+    if (def.rescale_count && overlaps(def.rescale_count, l_bytes, ins[i], in_bytes[i]))
       return fail(ATTN_ERR_ALIAS, "rescale_count overlaps an input");
   }
   if (overlaps(o, o_bytes, lse, l_bytes)) return fail(ATTN_ERR_ALIAS, "o overlaps lse");
@@ -158,9 +146,9 @@ attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const 
   return ATTN_OK;
 }
 
-attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                          int N, int d, int causal, float scale, const attn_fwd_opts* opts, void* stream) {
-  const attn_status_t st = attn_fwd_check(q, k, v, o, lse, B, H, N, d, causal, scale, opts);
+attn_status_t run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+                  int d, int causal, float scale, const attn_fwd_opts* opts, void* stream) {
+  const attn_status_t st = check_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, opts);
   if (st != ATTN_OK) return st;
   if ((int64_t)B * H * N == 0) return ATTN_OK;
   attn_fwd_opts o2;
@@ -175,6 +163,8 @@ attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   p.lse = lse;
   p.rescale_count = o2.rescale_count;
   p.N = N;
+  p.H = H;
+  p.G = H / Hkv;
   p.nq_tiles = (N + kRows - 1) / kRows;
   p.total_tiles = B * H * p.nq_tiles;
   p.per_xcd = (p.total_tiles + 7) / 8;
@@ -193,6 +183,45 @@ attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, 
                : launch_d<64>(p, causal != 0, of32, o2.exp2_poly_eighths, neg, (hipStream_t)stream);
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void attn_fwd_opts_init(attn_fwd_opts* opts) {
+  if (!opts) return;
+  memset(opts, 0, sizeof *opts);
+  opts->struct_size = sizeof *opts;
+  opts->rescale_tau_log2 = 8.0f;
+  opts->exp2_poly_eighths = 0;
+  opts->o_dtype = ATTN_O_BF16;
+  opts->rescale_count = nullptr;
+}
+
+attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, int B, int H, int N, int d, int causal,
+                             float scale, const attn_fwd_opts* opts) {
+  (void)causal;
+  return check_impl(q, k, v, o, lse, B, H, H, N, d, scale, opts);
+}
+
+attn_status_t attn_fwd_gqa_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                 int B, int H, int Hkv, int N, int d, int causal, float scale,
+                                 const attn_fwd_opts* opts) {
+  (void)causal;
+  return check_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, opts);
+}
+
+attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                          int N, int d, int causal, float scale, const attn_fwd_opts* opts, void* stream) {
+  return run(q, k, v, o, lse, B, H, H, N, d, causal, scale, opts, stream);
+}
+
+attn_status_t attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                           int Hkv, int N, int d, int causal, float scale, const attn_fwd_opts* opts,
+                           void* stream) {
+  return run(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, opts, stream);
 }
 
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,

@@ -1,7 +1,8 @@
 // attn_fwd_kernel.h - tiled exact-attention forward kernel for gfx950 (MI355X).
 //
 // One workgroup computes 256 query rows of one (batch, head); each of its 8
-// wavefronts owns 32 rows. The keys and values stream through LDS in
+// wavefronts owns 32 rows. With grouped-query attention the head's keys and
+// values are those of the key/value head its group of query heads shares. The keys and values stream through LDS in
 // tiles of BC rows, the queries stay in registers, and per query row the kernel
 // keeps a running maximum and running sum, so the N x N score matrix never
 // leaves the chip (page "Flash Attention" glossary, sections "Tiling with SRAM"
@@ -81,6 +82,8 @@ struct Params {
   float* lse;
   int* rescale_count;  // optional [B][H][N] int32
   int N;
+  int H;               // query heads
+  int G;               // query heads per key/value head (H / Hkv; 1 = multi-head)
   int nq_tiles;        // ceil(N / BR)
   int total_tiles;     // B * H * nq_tiles
   int per_xcd;         // ceil(total_tiles / 8): workgroups per XCD slice
@@ -430,7 +433,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   // workgroup stays on its XCD's range); the next tile's Q, K_0, V_0 and K_1
   // loads are then issued before the current tile's epilogue.
   struct Tile {
-    int bh, i0, n_tiles, t_full;
+    int bh, kvh, i0, n_tiles, t_full;  // kvh: the (batch, key/value head) that bh reads
   };
   // Causal: a persistent workgroup's successive tiles alternate direction
   // through its XCD's range (round r of S slots takes position i or S-1-i). The
@@ -448,6 +451,9 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     const int logical = (v & 7) * p.per_xcd + j;
     if (j >= p.per_xcd || logical >= p.total_tiles) return false;
     t.bh = logical / p.nq_tiles;
+    // consecutive groups of G query heads share a key/value head: b*H + h -> b*(H/G) + h/G
+    const int b = t.bh / p.H, h = t.bh - b * p.H;
+    t.kvh = b * (p.H / p.G) + h / p.G;
     int qt = logical - t.bh * p.nq_tiles;
     if (CAUSAL) qt = p.nq_tiles - 1 - qt;  // longest rows first
     t.i0 = qt * BR;
@@ -460,10 +466,11 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   bf16x8 qreg[KK];
   auto issue_loads = [&](const Tile& t) {
     const size_t head = (size_t)t.bh * (size_t)N * D;
+    const size_t kvhead = (size_t)t.kvh * (size_t)N * D;
     if (grp == 1) {  // n_tiles >= 1
-      load_tile<D, BC, 4>(koff, p.k + head, N, 0, kbuf0, wave & 3, true);
-      load_tile<D, BC, 4>(voff, p.v + head, N, 0, vbuf0, wave & 3, true);
-      load_tile<D, BC, 4>(koff, p.k + head, N, BC, kbuf1, wave & 3, t.n_tiles > 1);
+      load_tile<D, BC, 4>(koff, p.k + kvhead, N, 0, kbuf0, wave & 3, true);
+      load_tile<D, BC, 4>(voff, p.v + kvhead, N, 0, vbuf0, wave & 3, true);
+      load_tile<D, BC, 4>(koff, p.k + kvhead, N, BC, kbuf1, wave & 3, t.n_tiles > 1);
     }
     const __amdgpu_buffer_rsrc_t qrsrc = buffer_rsrc(p.q + head, head_bytes);
     const int q_row = t.i0 + wave * 32 + l32;
@@ -485,8 +492,9 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   const size_t head = (size_t)bh * (size_t)N * D;
   const int wq0 = i0 + wave * 32;
   const int my_q = wq0 + l32;
-  const __bf16* const kh = p.k + head;
-  const __bf16* const vh = p.v + head;
+  const size_t kvhead = (size_t)tile.kvh * (size_t)N * D;
+  const __bf16* const kh = p.k + kvhead;
+  const __bf16* const vh = p.v + kvhead;
 
   RowState<D> st;
 #pragma unroll

@@ -43,12 +43,14 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+/* 1: attn_fwd, attn_fwd_ex, attn_fwd_check and helpers.
+ * 2: adds attn_fwd_gqa and attn_fwd_gqa_check (grouped-query attention). */
+#define ATTN_ABI_VERSION 2
 
 typedef enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL (with B*H*N > 0) */
-  ATTN_ERR_DIM = 2,         /* B, H or N negative, or sizes overflow the supported range */
+  ATTN_ERR_DIM = 2,         /* B, H or N negative, Hkv not a divisor of H, or sizes overflow */
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, or an unknown option value */
   ATTN_ERR_MISALIGNED = 4,  /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
   ATTN_ERR_SCALE = 5,       /* scale is not finite */
@@ -120,6 +122,37 @@ attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, 
 attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const void* o,
                              const float* lse, int B, int H, int N, int d, int causal,
                              float scale, const attn_fwd_opts* opts);
+
+/*
+ * attn_fwd_gqa - grouped-query (and multi-query) attention forward: several
+ * query heads share one key/value head (page "FlashAttention 4: faster, more
+ * memory-efficient attention for LLMs", sections "Key points" and
+ * "Compatibility and current status", which list GQA/MQA among the
+ * configurations of earlier FlashAttention versions).
+ *   q       : const bf16 [B][H][N][d], device, 16-byte aligned.
+ *   k, v    : const bf16 [B][Hkv][N][d], device, 16-byte aligned.
+ *   o, lse  : as for attn_fwd ([B][H][N][d] and [B][H][N]).
+ *   Hkv     : key/value heads, 1 <= Hkv <= H and H % Hkv == 0 (0 when H == 0),
+ *             else ATTN_ERR_DIM. Query head h reads key/value head
+ *             h / (H / Hkv) (consecutive groups of H / Hkv query heads):
+ *
+ *     s_ij = scale * sum_c q[b,h,i,c] * k[b, h/(H/Hkv), j, c]   (v likewise)
+ *
+ *             Hkv = 1 is multi-query attention; Hkv = H is attn_fwd_ex,
+ *             bit for bit.
+ * Every other argument, the error behaviour and the asynchrony are those of
+ * attn_fwd_ex. The kernel and the tile walk are the same; the query heads of
+ * one group run next to each other, so their shared K and V tiles are
+ * fetched from HBM about once per group.
+ */
+attn_status_t attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Hkv, int N, int d, int causal, float scale,
+                           const attn_fwd_opts* opts, void* stream);
+
+/* Host-only argument check of attn_fwd_gqa (never touches the device). */
+attn_status_t attn_fwd_gqa_check(const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, int B, int H, int Hkv, int N, int d,
+                                 int causal, float scale, const attn_fwd_opts* opts);
 
 /* Tile shape the kernel uses for head dim d: query rows per workgroup and keys
  * per KV tile (the granularity of the online softmax and of the rescale

@@ -70,7 +70,10 @@ def sample_picks(B, H, N, seed, full_heads=((0, 0),), block=(32, 64, 128)):
 
 
 def check_sampled(q, k, v, causal, scale, o, lse, picks, what, tol_o=TOL_O, tol_lse=TOL_LSE):
-    refs = oracle.attention_rows(q, k, v, causal, scale, picks)
+    if k.shape[1] == q.shape[1]:
+        refs = oracle.attention_rows(q, k, v, causal, scale, picks)
+    else:
+        refs = oracle.attention_gqa_rows(q, k, v, causal, scale, picks)
     eo = el = 0.0
     for (b, h, rows), (o_ref, l_ref) in zip(picks, refs):
         eo = max(eo, max_err(o[b, h, rows], o_ref))

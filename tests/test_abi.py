@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(bnd.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == bnd.ABI_VERSION == 2
 
 
 def check(*args, **kw):
@@ -137,3 +137,40 @@ def test_exp2_polynomial_error_bound():
     ylo = np.empty_like(lo)
     lib.attn_exp2_poly_host(lo.ctypes.data, ylo.ctypes.data, lo.size)
     assert np.all(ylo >= 0) and np.all(ylo < 1e-37)
+
+
+def gqa_check(*args, **kw):
+    return bnd.attn_fwd_gqa_check(*args, **kw)
+
+
+def test_gqa_valid_arguments_pass():
+    for Hkv in (1, 2, 4, 8, 16, 32):
+        assert gqa_check(Q, K, V, O, L, 2, 32, Hkv, 8192, 128, 1, 0.088) == bnd.ATTN_OK
+    assert gqa_check(None, None, None, None, None, 1, 0, 0, 16, 64, 0, 1.0) == bnd.ATTN_OK
+    assert gqa_check(None, None, None, None, None, 0, 4, 2, 16, 64, 0, 1.0) == bnd.ATTN_OK
+    assert bnd.attn_fwd_gqa(None, None, None, None, None, 1, 4, 2, 0, 64, 0, 1.0, None, None) == bnd.ATTN_OK
+
+
+@pytest.mark.parametrize("H,Hkv", [(32, 0), (32, 3), (32, 64), (6, 4), (4, -1), (0, 1)])
+def test_gqa_bad_head_counts(H, Hkv):
+    assert gqa_check(Q, K, V, O, L, 1, H, Hkv, 8, 64, 0, 1.0) == 2
+    assert "Hkv" in bnd.last_error()
+    assert bnd.attn_fwd_gqa(Q, K, V, O, L, 1, H, Hkv, 8, 64, 0, 1.0, None, None) == 2
+
+
+def test_gqa_alias_uses_key_value_extent():
+    """k and v span B*Hkv*N*d elements: an output just past that extent is accepted."""
+    B, H, Hkv, N, d = 1, 8, 2, 64, 64
+    kv_bytes = B * Hkv * N * d * 2
+    assert gqa_check(Q, K, V, K + kv_bytes, L, B, H, Hkv, N, d, 0, 1.0) == bnd.ATTN_OK
+    assert gqa_check(Q, K, V, K + kv_bytes - 16, L, B, H, Hkv, N, d, 0, 1.0) == 6
+    # the MHA check uses the query extent for k, so the same o overlaps there
+    assert check(Q, K, V, K + kv_bytes, L, B, H, N, d, 0, 1.0) == 6
+
+
+def test_gqa_same_codes_as_mha_when_heads_equal():
+    cases = [(Q, K, V, O, L, 1, 4, 8, 96, 0, 1.0), (Q + 8, K, V, O, L, 1, 4, 8, 64, 0, 1.0),
+             (Q, K, V, O, L, 1, 4, 8, 64, 0, math.inf), (Q, K, V, Q, L, 1, 4, 8, 64, 0, 1.0)]
+    for a in cases:
+        g = a[:6] + (a[6],) + a[6:]
+        assert check(*a) == gqa_check(*g) != bnd.ATTN_OK
