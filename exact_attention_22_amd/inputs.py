@@ -16,6 +16,13 @@ Workloads (B heads-batch, H heads, N tokens, d head dim), all i.i.d. N(0,1):
             running row maximum keeps rising along the keys.
   gqa8k     2 x 32 x  8192 x 128  causal, grouped-query: 8 key/value heads,
             each shared by 4 consecutive query heads (k, v are [2, 8, 8192, 128]).
+
+Variable-length batches (`draw_varlen`): sequences packed along the token axis
+of a [H, total, d] tensor (k, v: [Hkv, total, d]) with cumulative lengths
+cu_seqlens. `varlen_lengths` draws B lengths log-uniformly between lo and hi
+(integers, so most are not multiples of any tile size).
+  varlen    24 sequences of 64 .. 8192 tokens (seed 1007), 32 query heads,
+            8 key/value heads, d = 128, causal.
 """
 from __future__ import annotations
 
@@ -87,6 +94,66 @@ def draw_gqa(B: int, H: int, Hkv: int, N: int, d: int, seed: int, drift: bool = 
         k += drift_rate * j * u
         q += u
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def varlen_lengths(B: int, lo: int, hi: int, seed: int) -> list[int]:
+    """B sequence lengths, log-uniform on [lo, hi], from one seed."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    u = torch.rand((B,), generator=g, dtype=torch.float64)
+    return [int(round(math.exp(math.log(lo) + x * (math.log(hi) - math.log(lo))))) for x in u.tolist()]
+
+
+def cu_seqlens(lengths) -> torch.Tensor:
+    """Cumulative lengths [0, l0, l0+l1, ...] as an int32 CPU tensor."""
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + int(n))
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+def draw_varlen(lengths, H: int, Hkv: int, d: int, seed: int):
+    """Packed sequences: q [H,total,d], k, v [Hkv,total,d] bf16 CPU tensors (drawn in
+    that order, N(0,1) in fp32, rounded once) and cu_seqlens (int32 [B+1])."""
+    cu = cu_seqlens(lengths)
+    T = int(cu[-1])
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((H, T, d), generator=g, dtype=torch.float32)
+    k = torch.randn((Hkv, T, d), generator=g, dtype=torch.float32)
+    v = torch.randn((Hkv, T, d), generator=g, dtype=torch.float32)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16), cu
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    B: int
+    lo: int
+    hi: int
+    H: int
+    Hkv: int
+    d: int
+    causal: bool
+    seed: int
+
+    @property
+    def lengths(self) -> list[int]:
+        return varlen_lengths(self.B, self.lo, self.hi, self.seed)
+
+    @property
+    def scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32).item())
+
+    @property
+    def flops(self) -> float:
+        """Sum over sequences of 4*H*n^2*d, halved for causal."""
+        f = sum(4.0 * self.H * n * n * self.d for n in self.lengths)
+        return f / 2.0 if self.causal else f
+
+    def inputs(self, seed: int | None = None):
+        return draw_varlen(self.lengths, self.H, self.Hkv, self.d, self.seed if seed is None else seed)
+
+
+VARLEN = VarlenWorkload("varlen", 24, 64, 8192, 32, 8, 128, True, 1007)
 
 
 def workload_inputs(w: Workload, seed: int | None = None):

@@ -14,4 +14,7 @@ from .exact import (  # noqa: F401
     attention_gqa_rows,
     brute_force_attention_gqa,
     kv_head,
+    attention_varlen,
+    attention_varlen_rows,
+    brute_force_attention_varlen,
 )

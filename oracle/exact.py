@@ -32,6 +32,16 @@ here is consecutive groups: with H query heads and Hkv key/value heads (Hkv
 divides H), query head h reads key/value head floor(h / (H / Hkv)). MQA is
 Hkv = 1; Hkv = H is ordinary multi-head attention.
 
+Variable-length batches (`attention_varlen`): several sequences of different
+lengths packed along the token axis, the other feature [LK] "Key points" lists
+as missing from FA4. The pages give no layout; the reading used here is the
+dense layout with the batch folded into the token axis: q is [H, total, d],
+k and v are [Hkv, total, d], and sequence b owns tokens cu[b] .. cu[b+1]-1 of
+every head (cu = cumulative lengths, cu[0] = 0, cu[B] = total). A query attends
+only to the keys of its own sequence; the causal mask compares positions inside
+the sequence. Query and key sequences share the same bounds (self-attention).
+LSE is [H, total].
+
 `tiled_online_attention` is a second, test-only float64 model that follows the
 algorithm the pages describe: tiles of queries and keys, a running maximum and
 running sum per query row ([JG] "Online softmax and recomputation";
@@ -148,6 +158,64 @@ def attention_gqa_rows(q, k, v, causal: bool, scale: float, picks):
     return out
 
 
+def _check_varlen(q, k, v, cu):
+    if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape:
+        raise ValueError(f"expected q [H,total,d] and k, v [Hkv,total,d], got {q.shape} {k.shape} {v.shape}")
+    H, T, d = q.shape
+    if k.shape[1] != T or k.shape[2] != d or k.shape[0] < 1 or H % k.shape[0]:
+        raise ValueError(f"key/value shape {k.shape} does not fit queries {q.shape}")
+    cu = np.asarray(cu, dtype=np.int64).reshape(-1)
+    if cu.size < 1 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError(f"cu_seqlens must start at 0, not decrease and end at total={T}: {cu.tolist()[:8]}...")
+    return cu
+
+
+def attention_varlen(q, k, v, cu_seqlens, causal: bool, scale: float, row_block: int = 1024):
+    """Exact attention over packed variable-length sequences, float64.
+
+    q: [H,total,d]; k, v: [Hkv,total,d] (Hkv divides H; query head h reads key/value
+    head h // (H // Hkv)); cu_seqlens: B+1 cumulative lengths. Each sequence is the
+    definition above on its own rows and keys. Returns (O[H,total,d], LSE[H,total]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = _check_varlen(q, k, v, cu_seqlens)
+    scale = float(np.float64(scale))
+    H, T, d = q.shape
+    Hkv = k.shape[0]
+    o = np.empty((H, T, d))
+    lse = np.empty((H, T))
+    for b in range(cu.size - 1):
+        a, e = int(cu[b]), int(cu[b + 1])
+        for h in range(H):
+            g = kv_head(h, H, Hkv)
+            for r0 in range(0, e - a, row_block):
+                rows = np.arange(r0, min(e - a, r0 + row_block))
+                o[h, a + rows], lse[h, a + rows] = _rows_of_head(q[h, a:e], k[g, a:e], v[g, a:e], rows, causal, scale)
+    return o, lse
+
+
+def attention_varlen_rows(q, k, v, cu_seqlens, causal: bool, scale: float, picks):
+    """`attention_varlen` at sampled outputs: picks = [(h, token indices)], tokens
+    in [0, total) (any sequences). Returns [(O[len,d], LSE[len])]."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64).reshape(-1)
+    scale = float(np.float64(scale))
+    H, Hkv = q.shape[0], k.shape[0]
+    out = []
+    for h, toks in picks:
+        toks = np.asarray(toks, dtype=np.int64)
+        g = kv_head(h, H, Hkv)
+        o = np.empty((toks.size, q.shape[2]))
+        lse = np.empty(toks.size)
+        seq = np.searchsorted(cu, toks, side="right") - 1   # sequence b with cu[b] <= t < cu[b+1]
+        for b in np.unique(seq):
+            a, e = int(cu[b]), int(cu[b + 1])
+            sel = seq == b
+            qh, kh, vh = _f64(q[h, a:e]), _f64(k[g, a:e]), _f64(v[g, a:e])
+            o[sel], lse[sel] = _rows_of_head(qh, kh, vh, toks[sel] - a, causal, scale)
+        out.append((o, lse))
+    return out
+
+
 def attention_rows(q, k, v, causal: bool, scale: float, picks):
     """Definition evaluated only at sampled outputs.
 
@@ -226,6 +294,37 @@ def brute_force_attention_gqa(q, k, v, causal: bool, scale: float):
                     for c in range(d):
                         o[b][h][i][c] = sum(wj * v[b][g][j][c] for wj, j in zip(w, keys)) / z
                     lse[b][h][i] = math.log(z)
+    return np.array(o), np.array(lse)
+
+
+def brute_force_attention_varlen(q, k, v, cu_seqlens, causal: bool, scale: float):
+    """Pure-Python loops over packed sequences (tiny inputs only), without the max
+    shift. Every (query token, key token) pair of a head is visited; a key counts
+    when both tokens lie in the same sequence (found by scanning the bounds) and,
+    if causal, the key does not come after the query."""
+    q, k, v = (_f64(t).tolist() for t in (q, k, v))
+    bounds = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    scale = float(np.float64(scale))
+    H, T, d = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(k)
+
+    def seq_of(t):
+        for b in range(len(bounds) - 1):
+            if bounds[b] <= t < bounds[b + 1]:
+                return b
+        raise ValueError(t)
+
+    o = [[[0.0] * d for _ in range(T)] for _ in range(H)]
+    lse = [[0.0] * T for _ in range(H)]
+    for h in range(H):
+        g = h * Hkv // H
+        for i in range(T):
+            keys = [j for j in range(T) if seq_of(j) == seq_of(i) and (not causal or j <= i)]
+            w = [math.exp(scale * sum(q[h][i][c] * k[g][j][c] for c in range(d))) for j in keys]
+            z = sum(w)
+            for c in range(d):
+                o[h][i][c] = sum(wj * v[g][j][c] for wj, j in zip(w, keys)) / z
+            lse[h][i] = math.log(z)
     return np.array(o), np.array(lse)
 
 
