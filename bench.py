@@ -52,6 +52,15 @@ def traffic_bytes(workload_name: str):
     return int((TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"] + TRAFFIC["write_kib"] * TRAFFIC["write_scale"]) * 1024)
 
 
+def describe(w) -> str:
+    from exact_attention_22_amd import inputs
+    if isinstance(w, inputs.VarlenWorkload):
+        L = w.lengths
+        return (f"{w.B} packed sequences of {min(L)}..{max(L)} tokens (total {sum(L)}) H={w.H} Hkv={w.Hkv} "
+                f"d={w.d}")
+    return f"B={w.B} H={w.H} Hkv={w.kv_heads} N={w.N} d={w.d}"
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -67,29 +76,51 @@ def parse():
     return ap.parse_args()
 
 
-def time_workload(w, steps, warmup, **kw):
-    """Average kernel time (ms) over `steps` launches, bracketed by device syncs,
-    measured with HIP events on the stream the kernel is launched on."""
+def workload_call(w, **kw):
+    """Device-resident inputs and outputs of a workload and a function that runs one
+    launch of the attention forward on them (dense or packed variable-length)."""
     import torch
 
     from exact_attention_22_amd import binding, inputs
 
     dev = torch.device("cuda:0")
-    q, k, v = (t.to(dev) for t in inputs.workload_inputs(w))
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    if isinstance(w, inputs.VarlenWorkload):
+        q, k, v, cu = (t.to(dev) for t in w.inputs())
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        max_seqlen = max(w.lengths)
+
+        def call():
+            binding.attention_varlen(q, k, v, cu, max_seqlen, causal=w.causal, scale=w.scale, out=o, lse=lse, **kw)
+    else:
+        q, k, v = (t.to(dev) for t in inputs.workload_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def call():
+            binding.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, **kw)
+    return call
+
+
+def time_workload(w, steps, warmup, **kw):
+    """Average kernel time (ms) over `steps` launches, bracketed by device syncs,
+    measured with HIP events on the stream the kernel is launched on."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    call = workload_call(w, **kw)
     for _ in range(warmup):
-        binding.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, **kw)
+        call()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(steps):
-        binding.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, **kw)
+        call()
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
-    del q, k, v, o, lse
+    del call
     torch.cuda.empty_cache()
     return ms
 
@@ -99,19 +130,15 @@ def time_samples(w, n_samples=20, min_ms=50.0):
     per-launch median and min (ms)."""
     import torch
 
-    from exact_attention_22_amd import binding, inputs
-
     dev = torch.device("cuda:0")
-    q, k, v = (t.to(dev) for t in inputs.workload_inputs(w))
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    call = workload_call(w)
     stream = torch.cuda.current_stream(dev)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def batch(n):
         start.record(stream)
         for _ in range(n):
-            binding.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            call()
         end.record(stream)
         torch.cuda.synchronize()
         return start.elapsed_time(end)
@@ -119,7 +146,7 @@ def time_samples(w, n_samples=20, min_ms=50.0):
     one = batch(3) / 3
     per_batch = max(1, int(math.ceil(min_ms / max(one, 1e-3))))
     ms = sorted(batch(per_batch) / per_batch for _ in range(n_samples))
-    del q, k, v, o, lse
+    del call
     torch.cuda.empty_cache()
     return {"n": n_samples, "launches_each": per_batch, "median_ms": round(ms[len(ms) // 2], 4),
             "min_ms": round(ms[0], 4)}
@@ -148,20 +175,31 @@ def cpu_baseline(w, target_s):
     import oracle
     from exact_attention_22_amd import inputs
 
-    q, k, v = inputs.draw(1, 1, w.N, w.d, seed=w.seed, drift=w.drift)
-    t0 = time.perf_counter()
-    oracle.attention(q, k, v, w.causal, w.scale)
-    one = time.perf_counter() - t0
-    heads = max(1, min(w.B * w.H, int(target_s / max(one, 1e-3))))
-    q, k, v = inputs.draw(1, heads, w.N, w.d, seed=w.seed + 1, drift=w.drift)
-    t0 = time.perf_counter()
-    oracle.attention(q, k, v, w.causal, w.scale)
-    dt = time.perf_counter() - t0
-    flops = w.flops / (w.B * w.H) * heads
+    if isinstance(w, inputs.VarlenWorkload):  # whole heads of the packed batch
+        units = w.H
+
+        def run(n, seed):
+            q, k, v, cu = inputs.draw_varlen(w.lengths, n, n, w.d, seed=seed)
+            t0 = time.perf_counter()
+            oracle.attention_varlen(q, k, v, cu, w.causal, w.scale)
+            return time.perf_counter() - t0
+    else:
+        units = w.B * w.H
+
+        def run(n, seed):
+            q, k, v = inputs.draw(1, n, w.N, w.d, seed=seed, drift=w.drift)
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, w.causal, w.scale)
+            return time.perf_counter() - t0
+
+    one = run(1, w.seed)
+    heads = max(1, min(units, int(target_s / max(one, 1e-3))))
+    dt = run(heads, w.seed + 1)
+    flops = w.flops / units * heads
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} heads of {w.name} (full rows), {dt:.1f} s fp64 numpy",
+            "sample": f"{heads} of {units} heads of {w.name} (full rows), {dt:.1f} s fp64 numpy",
             "seconds": round(dt, 2), "cpu_model": cpu_model(),
-            "full_workload_seconds_extrapolated": round(dt * w.B * w.H / heads, 1)}
+            "full_workload_seconds_extrapolated": round(dt * units / heads, 1)}
 
 
 def main():
@@ -178,8 +216,10 @@ def main():
         print("bench.py needs an MI355X (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(1)
     binding.lib()  # fail loudly if the HIP library is missing
-    w = inputs.BY_NAME[args.workload]
+    by_name = dict(inputs.BY_NAME, **{inputs.VARLEN.name: inputs.VARLEN})
+    w = by_name[args.workload]
 
+    is_varlen = isinstance(w, inputs.VarlenWorkload)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ms = time_workload(w, args.steps, args.warmup)
@@ -200,14 +240,14 @@ def main():
 
     others = {}
     if not args.no_others:
-        for o in inputs.WORKLOADS:
+        for o in by_name.values():
             if o.name == w.name:
                 continue
             oms = time_workload(o, max(5, args.steps // 2), max(3, args.warmup // 2))
             ot = o.flops / (oms * 1e-3) / 1e12
             others[o.name] = {"ms": round(oms, 4), "tflops": round(ot, 1),
                               "frac_peak": round(ot / PEAK_BF16_TFLOPS, 4), "causal": o.causal,
-                              "shape": [o.B, o.H, o.N, o.d], "kv_heads": o.kv_heads}
+                              "shape": describe(o)}
 
     line = {
         "metric": "attention fwd TFLOP/s (bf16, causal & non-causal) and % of MI355X MFMA peak",
@@ -222,9 +262,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: B={w.B} H={w.H} Hkv={w.kv_heads} N={w.N} d={w.d} "
-                               f"causal={w.causal} bf16 N(0,1) seed {w.seed}",
-                   "B": w.B, "H": w.H, "Hkv": w.kv_heads, "N": w.N, "d": w.d, "causal": w.causal},
+        "config": {"workload": f"{w.name}: {describe(w)} causal={w.causal} bf16 N(0,1) seed {w.seed}",
+                   "B": w.B, "H": w.H, "Hkv": w.Hkv if is_varlen else w.kv_heads,
+                   "N": max(w.lengths) if is_varlen else w.N, "d": w.d, "causal": w.causal},
         "frac_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),

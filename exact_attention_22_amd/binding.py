@@ -23,8 +23,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_DIM", 3: "ATTN_ERR_UNSU
 O_BF16, O_F32 = 0, 1
 EXPORTS = ["attn_fwd", "attn_fwd_ex", "attn_fwd_check", "attn_fwd_opts_init", "attn_status_str",
            "attn_last_error", "attn_abi_version", "attn_exp2_poly_host", "attn_fwd_tile_shape",
-           "attn_fwd_gqa", "attn_fwd_gqa_check"]
-ABI_VERSION = 2
+           "attn_fwd_gqa", "attn_fwd_gqa_check", "attn_fwd_varlen", "attn_fwd_varlen_check"]
+ABI_VERSION = 3
 
 
 class AttnFwdOpts(ctypes.Structure):
@@ -62,6 +62,11 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_gqa.restype = i
         L.attn_fwd_gqa_check.argtypes = gqa_args
         L.attn_fwd_gqa_check.restype = i
+        varlen_args = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, ctypes.POINTER(AttnFwdOpts)]
+        L.attn_fwd_varlen.argtypes = varlen_args + [vp]
+        L.attn_fwd_varlen.restype = i
+        L.attn_fwd_varlen_check.argtypes = varlen_args
+        L.attn_fwd_varlen_check.restype = i
         L.attn_fwd_opts_init.argtypes = [ctypes.POINTER(AttnFwdOpts)]
         L.attn_fwd_opts_init.restype = None
         L.attn_status_str.argtypes = [i]
@@ -129,6 +134,19 @@ def attn_fwd_gqa_check(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, opts: At
                                     ctypes.byref(opts) if opts is not None else None)
 
 
+def attn_fwd_varlen(q: int, k: int, v: int, o: int, lse: int, cu: int, B: int, H: int, Hkv: int, total: int,
+                    max_seqlen: int, d: int, causal: int, scale: float, opts: AttnFwdOpts | None,
+                    stream: int | None) -> int:
+    return lib().attn_fwd_varlen(q, k, v, o, lse, cu, B, H, Hkv, total, max_seqlen, d, int(causal), scale,
+                                 ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def attn_fwd_varlen_check(q, k, v, o, lse, cu, B, H, Hkv, total, max_seqlen, d, causal, scale,
+                          opts: AttnFwdOpts | None = None) -> int:
+    return lib().attn_fwd_varlen_check(q, k, v, o, lse, cu, B, H, Hkv, total, max_seqlen, d, int(causal), scale,
+                                       ctypes.byref(opts) if opts is not None else None)
+
+
 def _check_tensor(name, t, shape=None):
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
@@ -176,6 +194,54 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     else:
         st = attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           B, H, Hkv, N, d, causal, scale, opts, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, last_error())
+    return (out, lse, counts) if rescale_count else (out, lse)
+
+
+def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                     max_seqlen: int | None = None, causal: bool = False, scale: float | None = None, *,
+                     tau: float = 8.0, poly_eighths: int = 0, out_dtype: torch.dtype = torch.bfloat16,
+                     out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                     rescale_count: bool = False):
+    """Attention over packed variable-length sequences on the current stream.
+
+    q: bfloat16 [H,total,d]; k, v: bfloat16 [Hkv,total,d]; cu_seqlens: int32 [B+1]
+    device tensor of cumulative lengths (0, ..., total). max_seqlen defaults to the
+    longest sequence, read back from cu_seqlens (one device-to-host copy). Returns
+    (O [H,total,d], LSE [H,total][, rescale counts]).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 CUDA (HIP) tensor")
+        if t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [heads,total,d] tensor, got {tuple(t.shape)}")
+    H, T, d = q.shape
+    Hkv = k.shape[0]
+    if tuple(k.shape) != (Hkv, T, d) or tuple(v.shape) != (Hkv, T, d):
+        raise ValueError(f"k and v must be [Hkv,{T},{d}], got {tuple(k.shape)} {tuple(v.shape)}")
+    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous()):
+        raise TypeError("cu_seqlens must be a contiguous int32 [B+1] tensor on q's device")
+    B = cu_seqlens.numel() - 1
+    if B < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if B > 0 else 0
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((H, T, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    counts = torch.empty((H, T), dtype=torch.int32, device=q.device) if rescale_count else None
+    opts = make_opts(tau, poly_eighths, O_F32 if out_dtype == torch.float32 else O_BF16,
+                     counts.data_ptr() if counts is not None else None)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         cu_seqlens.data_ptr(), B, H, Hkv, T, max_seqlen, d, causal, scale, opts, stream)
     if st != ATTN_OK:
         raise AttnError(st, last_error())
     return (out, lse, counts) if rescale_count else (out, lse)

@@ -59,8 +59,14 @@ int cus_per_xcd() {
   return v;
 }
 
+template <int D, bool CAUSAL, bool OF32, int POLY8, bool NEG>
+const void* kernel_fn(bool varlen) {
+  return varlen ? reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, OF32, POLY8, NEG, true>)
+                : reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, OF32, POLY8, NEG, false>);
+}
+
 template <int D, bool CAUSAL, bool OF32, int POLY8>
-hipError_t launch(const attn::Params& p, bool neg, hipStream_t stream) {
+hipError_t launch(const attn::Params& p, bool neg, bool varlen, hipStream_t stream) {
   // hipLaunchKernel reports this launch's own error (no sticky state from other calls).
   // A negative scale flips the row maximum of s*c into c * min(s): separate instantiation.
   // One workgroup per compute unit walks its XCD's tile range, so the next tile's
@@ -70,119 +76,156 @@ hipError_t launch(const attn::Params& p, bool neg, hipStream_t stream) {
   if (slots > 0 && slots < per_wg_xcd) per_wg_xcd = slots;
   const dim3 grid(per_wg_xcd * 8), block(64 * kWaves);
   void* args[] = {const_cast<attn::Params*>(&p)};
-  const void* fn = neg ? reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, OF32, POLY8, true>)
-                       : reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, OF32, POLY8, false>);
+  const void* fn = neg ? kernel_fn<D, CAUSAL, OF32, POLY8, true>(varlen) : kernel_fn<D, CAUSAL, OF32, POLY8, false>(varlen);
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 template <int D, bool CAUSAL, bool OF32>
-hipError_t launch_poly(const attn::Params& p, int poly8, bool neg, hipStream_t s) {
+hipError_t launch_poly(const attn::Params& p, int poly8, bool neg, bool varlen, hipStream_t s) {
   switch (poly8) {
-    case 0: return launch<D, CAUSAL, OF32, 0>(p, neg, s);
-    case 4: return launch<D, CAUSAL, OF32, 4>(p, neg, s);
-    default: return launch<D, CAUSAL, OF32, 8>(p, neg, s);
+    case 0: return launch<D, CAUSAL, OF32, 0>(p, neg, varlen, s);
+    case 4: return launch<D, CAUSAL, OF32, 4>(p, neg, varlen, s);
+    default: return launch<D, CAUSAL, OF32, 8>(p, neg, varlen, s);
   }
 }
 
 template <int D>
-hipError_t launch_d(const attn::Params& p, bool causal, bool of32, int poly8, bool neg, hipStream_t s) {
+hipError_t launch_d(const attn::Params& p, bool causal, bool of32, int poly8, bool neg, bool varlen, hipStream_t s) {
   if (causal)
-    return of32 ? launch_poly<D, true, true>(p, poly8, neg, s) : launch_poly<D, true, false>(p, poly8, neg, s);
-  return of32 ? launch_poly<D, false, true>(p, poly8, neg, s) : launch_poly<D, false, false>(p, poly8, neg, s);
+    return of32 ? launch_poly<D, true, true>(p, poly8, neg, varlen, s)
+                : launch_poly<D, true, false>(p, poly8, neg, varlen, s);
+  return of32 ? launch_poly<D, false, true>(p, poly8, neg, varlen, s)
+              : launch_poly<D, false, false>(p, poly8, neg, varlen, s);
 }
 
-attn_status_t check_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
-                         int H, int Hkv, int N, int d, float scale, const attn_fwd_opts* opts) {
+// One call, dense ([B][H][N][d]) or packed (varlen: [H][total][d] with cu_seqlens).
+struct Problem {
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  const int* cu;   // packed only
+  bool varlen;
+  int B, H, Hkv;   // B: batch (dense) or number of sequences (packed)
+  int N;           // dense: sequence length; packed: total tokens per head
+  int max_seqlen;  // packed only
+  int d;
+  float scale;
+};
+
+// Host-side validation shared by every entry point (never touches the device).
+// On success *def holds the options in effect and *work whether anything is to be done.
+attn_status_t validate(const Problem& P, const attn_fwd_opts* opts, attn_fwd_opts* def, bool* work) {
   g_last_error[0] = '\0';
-  attn_fwd_opts def;
-  attn_fwd_opts_init(&def);
+  *work = false;
+  attn_fwd_opts_init(def);
   if (opts) {
     if (opts->struct_size < sizeof(attn_fwd_opts))
       return fail(ATTN_ERR_OPTS, "opts->struct_size %zu < %zu", opts->struct_size, sizeof(attn_fwd_opts));
-    def = *opts;
+    *def = *opts;
   }
+  const int B = P.B, H = P.H, Hkv = P.Hkv, N = P.N, d = P.d;
   if (B < 0 || H < 0 || N < 0) return fail(ATTN_ERR_DIM, "negative size B=%d H=%d N=%d", B, H, N);
+  if (P.varlen && P.max_seqlen < 0) return fail(ATTN_ERR_DIM, "negative max_seqlen %d", P.max_seqlen);
   if (H > 0 ? (Hkv < 1 || Hkv > H || H % Hkv != 0) : Hkv != 0)
     return fail(ATTN_ERR_DIM, "key/value heads Hkv=%d must divide query heads H=%d", Hkv, H);
   if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
-  if (!isfinite(scale)) return fail(ATTN_ERR_SCALE, "scale is not finite");
-  if (!(def.rescale_tau_log2 >= 0.f && def.rescale_tau_log2 <= 64.f))
-    return fail(ATTN_ERR_OPTS, "rescale_tau_log2 %g outside [0, 64]", (double)def.rescale_tau_log2);
-  if (def.exp2_poly_eighths != 0 && def.exp2_poly_eighths != 4 && def.exp2_poly_eighths != 8)
-    return fail(ATTN_ERR_UNSUPPORTED, "exp2_poly_eighths %d (supported: 0, 4, 8)", def.exp2_poly_eighths);
-  if (def.o_dtype != ATTN_O_BF16 && def.o_dtype != ATTN_O_F32)
-    return fail(ATTN_ERR_UNSUPPORTED, "o_dtype %d", def.o_dtype);
-  if ((int64_t)B * H * N == 0) return ATTN_OK;  // empty: nothing to do
+  if (!isfinite(P.scale)) return fail(ATTN_ERR_SCALE, "scale is not finite");
+  if (!(def->rescale_tau_log2 >= 0.f && def->rescale_tau_log2 <= 64.f))
+    return fail(ATTN_ERR_OPTS, "rescale_tau_log2 %g outside [0, 64]", (double)def->rescale_tau_log2);
+  if (def->exp2_poly_eighths != 0 && def->exp2_poly_eighths != 4 && def->exp2_poly_eighths != 8)
+    return fail(ATTN_ERR_UNSUPPORTED, "exp2_poly_eighths %d (supported: 0, 4, 8)", def->exp2_poly_eighths);
+  if (def->o_dtype != ATTN_O_BF16 && def->o_dtype != ATTN_O_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "o_dtype %d", def->o_dtype);
+  // longest sequence a query tile walk has to cover
+  const int64_t seq = P.varlen ? (P.max_seqlen < N ? P.max_seqlen : N) : N;
+  if ((int64_t)B * H * seq == 0) return ATTN_OK;  // empty: nothing to do
 
-  const int64_t rows = (int64_t)B * H * N;
-  const int64_t tiles = (int64_t)B * H * ((N + kRows - 1) / kRows);
+  // output rows: B*H*N (dense) or H*total (packed)
+  const int64_t rows = P.varlen ? (int64_t)H * N : (int64_t)B * H * N;
+  const int64_t tiles = (int64_t)B * H * ((seq + kRows - 1) / kRows);
   if (rows > (int64_t)1 << 40 || tiles + 8 > INT32_MAX)
-    return fail(ATTN_ERR_DIM, "problem too large: B*H*N=%lld", (long long)rows);
-  // one head's tensor (plus one tile of padding rows) is addressed with 32-bit byte offsets
-  if ((int64_t)(N + 256) * d * 2 > INT32_MAX) return fail(ATTN_ERR_DIM, "N=%d too long for one head", N);
-  if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_NULL, "NULL tensor pointer");
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
+    return fail(ATTN_ERR_DIM, "problem too large: %lld rows, %lld tiles", (long long)rows, (long long)tiles);
+  // one head's rows (plus one tile of padding rows) are addressed with 32-bit byte
+  // offsets; packed: the whole token axis, so that no contents of cu_seqlens can
+  // take an offset past that range
+  if ((int64_t)(N + 256) * d * 2 > INT32_MAX)
+    return fail(ATTN_ERR_DIM, "%s=%d too long for 32-bit row offsets", P.varlen ? "total" : "N", N);
+  if (!P.q || !P.k || !P.v || !P.o || !P.lse || (P.varlen && !P.cu))
+    return fail(ATTN_ERR_NULL, "NULL tensor pointer");
+  if (((uintptr_t)P.q | (uintptr_t)P.k | (uintptr_t)P.v | (uintptr_t)P.o) & 15)
     return fail(ATTN_ERR_MISALIGNED, "q, k, v and o must be 16-byte aligned");
-  if ((uintptr_t)lse & 3) return fail(ATTN_ERR_MISALIGNED, "lse must be 4-byte aligned");
-  if (def.rescale_count && ((uintptr_t)def.rescale_count & 3))
+  if ((uintptr_t)P.lse & 3) return fail(ATTN_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  if (P.varlen && ((uintptr_t)P.cu & 3)) return fail(ATTN_ERR_MISALIGNED, "cu_seqlens must be 4-byte aligned");
+  if (def->rescale_count && ((uintptr_t)def->rescale_count & 3))
     return fail(ATTN_ERR_MISALIGNED, "rescale_count must be 4-byte aligned");
 
   const size_t q_bytes = (size_t)rows * d * 2;
-  const size_t kv_bytes = (size_t)B * Hkv * N * d * 2;
-  const size_t o_bytes = (size_t)rows * d * (def.o_dtype == ATTN_O_F32 ? 4 : 2);
+  const size_t kv_bytes = (size_t)rows / H * Hkv * d * 2;
+  const size_t o_bytes = (size_t)rows * d * (def->o_dtype == ATTN_O_F32 ? 4 : 2);
   const size_t l_bytes = (size_t)rows * 4;
-  const void* ins[3] = {q, k, v};
-  const size_t in_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
-  for (int i = 0; i < 3; ++i) {
-    if (overlaps(o, o_bytes, ins[i], in_bytes[i])) return fail(ATTN_ERR_ALIAS, "o overlaps an input");
-    if (overlaps(lse, l_bytes, ins[i], in_bytes[i])) return fail(ATTN_ERR_ALIAS, "lse overlaps an input");
-    if (def.rescale_count && overlaps(def.rescale_count, l_bytes, ins[i], in_bytes[i]))
+  const void* ins[4] = {P.q, P.k, P.v, P.cu};
+  const size_t in_bytes[4] = {q_bytes, kv_bytes, kv_bytes, P.varlen ? (size_t)(B + 1) * 4 : 0};
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(P.o, o_bytes, ins[i], in_bytes[i])) return fail(ATTN_ERR_ALIAS, "o overlaps an input");
+    if (overlaps(P.lse, l_bytes, ins[i], in_bytes[i])) return fail(ATTN_ERR_ALIAS, "lse overlaps an input");
+    if (def->rescale_count && overlaps(def->rescale_count, l_bytes, ins[i], in_bytes[i]))
       return fail(ATTN_ERR_ALIAS, "rescale_count overlaps an input");
   }
-  if (overlaps(o, o_bytes, lse, l_bytes)) return fail(ATTN_ERR_ALIAS, "o overlaps lse");
-  if (def.rescale_count &&
-      (overlaps(def.rescale_count, l_bytes, o, o_bytes) || overlaps(def.rescale_count, l_bytes, lse, l_bytes)))
+  if (overlaps(P.o, o_bytes, P.lse, l_bytes)) return fail(ATTN_ERR_ALIAS, "o overlaps lse");
+  if (def->rescale_count &&
+      (overlaps(def->rescale_count, l_bytes, P.o, o_bytes) || overlaps(def->rescale_count, l_bytes, P.lse, l_bytes)))
     return fail(ATTN_ERR_ALIAS, "rescale_count overlaps an output");
+  *work = true;
   return ATTN_OK;
 }
 
-attn_status_t run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
-                  int d, int causal, float scale, const attn_fwd_opts* opts, void* stream) {
-  const attn_status_t st = check_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, opts);
-  if (st != ATTN_OK) return st;
-  if ((int64_t)B * H * N == 0) return ATTN_OK;
+attn_status_t run(const Problem& P, int causal, const attn_fwd_opts* opts, void* stream) {
   attn_fwd_opts o2;
-  attn_fwd_opts_init(&o2);
-  if (opts) o2 = *opts;
+  bool work = false;
+  const attn_status_t st = validate(P, opts, &o2, &work);
+  if (st != ATTN_OK || !work) return st;
 
   attn::Params p;
-  p.q = (const __bf16*)q;
-  p.k = (const __bf16*)k;
-  p.v = (const __bf16*)v;
-  p.o = o;
-  p.lse = lse;
+  p.q = (const __bf16*)P.q;
+  p.k = (const __bf16*)P.k;
+  p.v = (const __bf16*)P.v;
+  p.o = P.o;
+  p.lse = P.lse;
   p.rescale_count = o2.rescale_count;
-  p.N = N;
-  p.H = H;
-  p.G = H / Hkv;
-  p.nq_tiles = (N + kRows - 1) / kRows;
-  p.total_tiles = B * H * p.nq_tiles;
+  p.cu_seqlens = P.varlen ? P.cu : nullptr;
+  p.nseq = P.varlen ? P.B : 0;
+  p.N = P.N;
+  p.H = P.H;
+  p.G = P.H / P.Hkv;
+  const int seq = P.varlen ? (P.max_seqlen < P.N ? P.max_seqlen : P.N) : P.N;
+  p.nq_tiles = (seq + kRows - 1) / kRows;
+  p.total_tiles = P.B * P.H * p.nq_tiles;
   p.per_xcd = (p.total_tiles + 7) / 8;
   // c = scale * log2(e) in fp32. Masked scores are set to -inf (+inf for a negative
   // scale) and rely on s*c - m = -inf; for scale == 0 that product would be NaN, so
   // 0 is replaced by 2^-100: |s| <= 2^17 for bf16 inputs with d <= 128, hence
   // |s*c| < 2^-82 and 2^(s*c - m) rounds to exactly 1.0f, as with c = 0.
-  p.c = scale * 1.44269504088896341f;
+  p.c = P.scale * 1.44269504088896341f;
   if (p.c == 0.f) p.c = 0x1p-100f;
   p.tau = o2.rescale_tau_log2;
 
   const bool of32 = o2.o_dtype == ATTN_O_F32;
-  const bool neg = scale < 0.f;
+  const bool neg = P.scale < 0.f;
   const hipError_t err =
-      d == 128 ? launch_d<128>(p, causal != 0, of32, o2.exp2_poly_eighths, neg, (hipStream_t)stream)
-               : launch_d<64>(p, causal != 0, of32, o2.exp2_poly_eighths, neg, (hipStream_t)stream);
+      P.d == 128 ? launch_d<128>(p, causal != 0, of32, o2.exp2_poly_eighths, neg, P.varlen, (hipStream_t)stream)
+                 : launch_d<64>(p, causal != 0, of32, o2.exp2_poly_eighths, neg, P.varlen, (hipStream_t)stream);
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
   return ATTN_OK;
+}
+
+Problem dense(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H, int Hkv,
+              int N, int d, float scale) {
+  return Problem{q, k, v, const_cast<void*>(o), const_cast<float*>(lse), nullptr, false, B, H, Hkv, N, 0, d, scale};
+}
+
+Problem packed(const void* q, const void* k, const void* v, const void* o, const float* lse, const int* cu, int B,
+               int H, int Hkv, int total, int max_seqlen, int d, float scale) {
+  return Problem{q, k, v, const_cast<void*>(o), const_cast<float*>(lse), cu, true, B, H, Hkv, total, max_seqlen, d, scale};
 }
 
 }  // namespace
@@ -203,25 +246,44 @@ attn_status_t attn_fwd_check(const void* q, const void* k, const void* v, const 
                              const float* lse, int B, int H, int N, int d, int causal,
                              float scale, const attn_fwd_opts* opts) {
   (void)causal;
-  return check_impl(q, k, v, o, lse, B, H, H, N, d, scale, opts);
+  attn_fwd_opts def;
+  bool work;
+  return validate(dense(q, k, v, o, lse, B, H, H, N, d, scale), opts, &def, &work);
 }
 
 attn_status_t attn_fwd_gqa_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                  int B, int H, int Hkv, int N, int d, int causal, float scale,
                                  const attn_fwd_opts* opts) {
   (void)causal;
-  return check_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, opts);
+  attn_fwd_opts def;
+  bool work;
+  return validate(dense(q, k, v, o, lse, B, H, Hkv, N, d, scale), opts, &def, &work);
+}
+
+attn_status_t attn_fwd_varlen_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                    const int* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen, int d,
+                                    int causal, float scale, const attn_fwd_opts* opts) {
+  (void)causal;
+  attn_fwd_opts def;
+  bool work;
+  return validate(packed(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d, scale), opts, &def, &work);
 }
 
 attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                           int N, int d, int causal, float scale, const attn_fwd_opts* opts, void* stream) {
-  return run(q, k, v, o, lse, B, H, H, N, d, causal, scale, opts, stream);
+  return run(dense(q, k, v, o, lse, B, H, H, N, d, scale), causal, opts, stream);
 }
 
 attn_status_t attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                            int Hkv, int N, int d, int causal, float scale, const attn_fwd_opts* opts,
                            void* stream) {
-  return run(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, opts, stream);
+  return run(dense(q, k, v, o, lse, B, H, Hkv, N, d, scale), causal, opts, stream);
+}
+
+attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen, int d,
+                              int causal, float scale, const attn_fwd_opts* opts, void* stream) {
+  return run(packed(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d, scale), causal, opts, stream);
 }
 
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,

@@ -80,12 +80,14 @@ struct Params {
   const __bf16* v;
   void* o;
   float* lse;
-  int* rescale_count;  // optional [B][H][N] int32
-  int N;
+  int* rescale_count;  // optional, one int32 per output row
+  const int* cu_seqlens;  // packed batches: nseq + 1 cumulative sequence lengths (device)
+  int nseq;            // packed batches: number of sequences
+  int N;               // rows of one head in memory: the sequence length, or the packed total
   int H;               // query heads
   int G;               // query heads per key/value head (H / Hkv; 1 = multi-head)
-  int nq_tiles;        // ceil(N / BR)
-  int total_tiles;     // B * H * nq_tiles
+  int nq_tiles;        // ceil(N / BR); packed batches: ceil(longest sequence / BR)
+  int total_tiles;     // B * H * nq_tiles; packed batches: H * nseq * nq_tiles
   int per_xcd;         // ceil(total_tiles / 8): workgroups per XCD slice
   float c;             // scale * log2(e) in fp32; +-2^-100 stands in for 0 (see the launcher)
   float tau;           // rescale threshold, log2 units
@@ -394,7 +396,12 @@ __device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 3
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <int D, int BC, bool CAUSAL, bool OF32, int POLY8, bool NEG>
+// VARLEN: packed variable-length batches. q and o are [H][total][D], k and v
+// [Hkv][total][D], lse [H][total]; sequence b owns tokens cu[b] .. cu[b+1]-1 of
+// every head and attends only to itself (causal positions counted from its
+// first token). Each tile reads its sequence's bounds; the buffer resources end
+// at the sequence's last row, so no load crosses into the next sequence.
+template <int D, int BC, bool CAUSAL, bool OF32, int POLY8, bool NEG, bool VARLEN>
 __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   constexpr int NW = 8;            // wavefronts per workgroup (2 per SIMD)
   constexpr int BR = 32 * NW;      // query rows per workgroup
@@ -434,6 +441,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   // loads are then issued before the current tile's epilogue.
   struct Tile {
     int bh, kvh, i0, n_tiles, t_full;  // kvh: the (batch, key/value head) that bh reads
+    int n, start;  // packed batches: the sequence's length and first token (bh, kvh: heads)
   };
   // Causal: a persistent workgroup's successive tiles alternate direction
   // through its XCD's range (round r of S slots takes position i or S-1-i). The
@@ -442,37 +450,67 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   // work, while the tiles running at the same time stay within few heads (their
   // K and V share the XCD's L2).
   const int S = (int)gridDim.x >> 3;  // workgroups per XCD
-  auto tile_of = [&](int v, Tile& t) -> bool {
+  // Packed batches: logical tile (h * nseq + b) * nq_tiles + qt, so an XCD's range
+  // holds whole heads with all their sequences (equal work per XCD when 8 divides
+  // H). Slots past a sequence's last query tile are empty (-1) and skipped.
+  // Returns 1 for a tile, -1 for an empty slot, 0 past the end of the range.
+  auto tile_of = [&](int v, Tile& t) -> int {
     int j = v >> 3;
     if (CAUSAL) {
       const int r = j / S, i = j - r * S;
       j = r * S + ((r & 1) ? S - 1 - i : i);
     }
     const int logical = (v & 7) * p.per_xcd + j;
-    if (j >= p.per_xcd || logical >= p.total_tiles) return false;
+    if (j >= p.per_xcd || logical >= p.total_tiles) return 0;
     t.bh = logical / p.nq_tiles;
-    // consecutive groups of G query heads share a key/value head: b*H + h -> b*(H/G) + h/G
-    const int b = t.bh / p.H, h = t.bh - b * p.H;
-    t.kvh = b * (p.H / p.G) + h / p.G;
     int qt = logical - t.bh * p.nq_tiles;
-    if (CAUSAL) qt = p.nq_tiles - 1 - qt;  // longest rows first
+    int n = N;
+    if (VARLEN) {
+      const int h = t.bh / p.nseq, b = t.bh - h * p.nseq;
+      // bounds clamped into [0, total]: any contents of cu keep every access in range
+      const int a = min(max(p.cu_seqlens[b], 0), N);
+      const int e = min(max(p.cu_seqlens[b + 1], a), N);
+      t.start = a;
+      t.n = n = e - a;
+      // a sequence longer than nq_tiles query tiles has its later rows left unwritten
+      const int nq = min((n + BR - 1) / BR, p.nq_tiles);
+      if (qt >= nq) return -1;
+      if (CAUSAL) qt = nq - 1 - qt;  // longest rows first
+      t.bh = h;
+      t.kvh = h / p.G;
+    } else {
+      // consecutive groups of G query heads share a key/value head: b*H + h -> b*(H/G) + h/G
+      const int b = t.bh / p.H, h = t.bh - b * p.H;
+      t.kvh = b * (p.H / p.G) + h / p.G;
+      if (CAUSAL) qt = p.nq_tiles - 1 - qt;  // longest rows first
+    }
     t.i0 = qt * BR;
-    const int kv_end = CAUSAL ? min(N, t.i0 + BR) : N;
+    const int kv_end = CAUSAL ? min(n, t.i0 + BR) : n;
     t.n_tiles = (kv_end + BC - 1) / BC;
-    t.t_full = N / BC;
+    t.t_full = n / BC;
     if (CAUSAL) t.t_full = min(t.t_full, (t.i0 + 1) / BC);
-    return true;
+    return 1;
+  };
+  // The first tile at or after slot v (advancing v past empty slots).
+  auto find_tile = [&](int& v, Tile& t) -> bool {
+    for (;;) {
+      const int r = tile_of(v, t);
+      if (!VARLEN || r >= 0) return r > 0;
+      v += (int)gridDim.x;
+    }
   };
   bf16x8 qreg[KK];
   auto issue_loads = [&](const Tile& t) {
-    const size_t head = (size_t)t.bh * (size_t)N * D;
-    const size_t kvhead = (size_t)t.kvh * (size_t)N * D;
+    const size_t head = VARLEN ? ((size_t)t.bh * N + t.start) * D : (size_t)t.bh * (size_t)N * D;
+    const size_t kvhead = VARLEN ? ((size_t)t.kvh * N + t.start) * D : (size_t)t.kvh * (size_t)N * D;
+    const int n = VARLEN ? t.n : N;
     if (grp == 1) {  // n_tiles >= 1
-      load_tile<D, BC, 4>(koff, p.k + kvhead, N, 0, kbuf0, wave & 3, true);
-      load_tile<D, BC, 4>(voff, p.v + kvhead, N, 0, vbuf0, wave & 3, true);
-      load_tile<D, BC, 4>(koff, p.k + kvhead, N, BC, kbuf1, wave & 3, t.n_tiles > 1);
+      load_tile<D, BC, 4>(koff, p.k + kvhead, n, 0, kbuf0, wave & 3, true);
+      load_tile<D, BC, 4>(voff, p.v + kvhead, n, 0, vbuf0, wave & 3, true);
+      load_tile<D, BC, 4>(koff, p.k + kvhead, n, BC, kbuf1, wave & 3, t.n_tiles > 1);
     }
-    const __amdgpu_buffer_rsrc_t qrsrc = buffer_rsrc(p.q + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t qrsrc =
+        buffer_rsrc(p.q + head, VARLEN ? (uint32_t)n * D * 2 : head_bytes);
     const int q_row = t.i0 + wave * 32 + l32;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
@@ -482,17 +520,19 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
 
   int slot = blockIdx.x;
   Tile tile;
-  if (!tile_of(slot, tile)) return;
+  if (!find_tile(slot, tile)) return;
   issue_loads(tile);
   for (;;) {
   const int bh = tile.bh;
   const int i0 = tile.i0;
   const int n_tiles = tile.n_tiles;
   const int t_full = tile.t_full;
-  const size_t head = (size_t)bh * (size_t)N * D;
+  // first output row of this (head, sequence) and the rows it has
+  const size_t row0 = VARLEN ? (size_t)bh * p.N + tile.start : (size_t)bh * p.N;
+  const int N = VARLEN ? tile.n : p.N;
   const int wq0 = i0 + wave * 32;
   const int my_q = wq0 + l32;
-  const size_t kvhead = (size_t)tile.kvh * (size_t)N * D;
+  const size_t kvhead = VARLEN ? ((size_t)tile.kvh * p.N + tile.start) * D : (size_t)tile.kvh * (size_t)N * D;
   const __bf16* const kh = p.k + kvhead;
   const __bf16* const vh = p.v + kvhead;
 
@@ -564,13 +604,14 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   // register is read again: the next tile's loads can go out now and land
   // while this tile's output is written.
   Tile next;
-  const bool more = tile_of(slot + (int)gridDim.x, next);
+  int next_slot = slot + (int)gridDim.x;
+  const bool more = find_tile(next_slot, next);
   if (more) issue_loads(next);
 
   const float l_tot = pair_sum(st.l_sum);
   if (my_q < N) {
     const float inv = 1.f / l_tot;
-    const size_t row = (size_t)bh * N + my_q;
+    const size_t row = row0 + my_q;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -595,7 +636,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   }
   if (!more) break;
   tile = next;
-  slot += (int)gridDim.x;
+  slot = next_slot;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
 }

@@ -44,8 +44,9 @@ extern "C" {
 #endif
 
 /* 1: attn_fwd, attn_fwd_ex, attn_fwd_check and helpers.
- * 2: adds attn_fwd_gqa and attn_fwd_gqa_check (grouped-query attention). */
-#define ATTN_ABI_VERSION 2
+ * 2: adds attn_fwd_gqa and attn_fwd_gqa_check (grouped-query attention).
+ * 3: adds attn_fwd_varlen and attn_fwd_varlen_check (packed variable-length batches). */
+#define ATTN_ABI_VERSION 3
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -153,6 +154,48 @@ attn_status_t attn_fwd_gqa(const void* q, const void* k, const void* v, void* o,
 attn_status_t attn_fwd_gqa_check(const void* q, const void* k, const void* v, const void* o,
                                  const float* lse, int B, int H, int Hkv, int N, int d,
                                  int causal, float scale, const attn_fwd_opts* opts);
+
+/*
+ * attn_fwd_varlen - attention over a packed batch of sequences of different
+ * lengths (page "FlashAttention 4: faster, more memory-efficient attention for
+ * LLMs", section "Key points", which lists variable-length batches among the
+ * features earlier FlashAttention versions had and FA4 lacked). Each sequence
+ * attends only to itself; query and key/value sequences share the same bounds
+ * (self-attention), and the causal mask counts positions from the sequence's
+ * first token. Grouped-query heads as for attn_fwd_gqa.
+ *   q, o       : bf16 [H][total][d] (o: float [H][total][d] with ATTN_O_F32),
+ *                device, 16-byte aligned: the dense layout with the batch
+ *                folded into the token axis.
+ *   k, v       : const bf16 [Hkv][total][d], device, 16-byte aligned.
+ *   lse        : float [H][total], device, 4-byte aligned.
+ *   cu_seqlens : const int32 [B + 1], DEVICE, 4-byte aligned: cumulative
+ *                lengths, cu[0] = 0, non-decreasing, cu[B] = total; sequence b
+ *                is tokens cu[b] .. cu[b+1]-1 of every head. Empty sequences
+ *                are allowed. The host cannot read it without synchronising,
+ *                so its contents are not validated: the kernel clamps every
+ *                bound into [0, total] (no access leaves the tensors whatever
+ *                it holds), but rows of an ill-formed array are not defined.
+ *   B          : number of sequences (>= 0).
+ *   total      : tokens per head (>= 0); (total + 256) * d * 2 < 2^31.
+ *   max_seqlen : >= the longest sequence (values above total are treated as
+ *                total); it sizes the launch. Rows of a sequence longer than
+ *                max_seqlen rounded up to a multiple of 256 are not written.
+ *   rescale_count option: int32 [H][total].
+ * B, H, total or max_seqlen of 0 return ATTN_OK and launch nothing. Other
+ * arguments, errors (cu_seqlens NULL: ATTN_ERR_NULL; outputs overlapping
+ * cu_seqlens: ATTN_ERR_ALIAS) and asynchrony as for attn_fwd_ex.
+ */
+attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int* cu_seqlens, int B, int H, int Hkv, int total,
+                              int max_seqlen, int d, int causal, float scale,
+                              const attn_fwd_opts* opts, void* stream);
+
+/* Host-only argument check of attn_fwd_varlen (never touches the device, so it
+ * does not read cu_seqlens). */
+attn_status_t attn_fwd_varlen_check(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const int* cu_seqlens, int B, int H,
+                                    int Hkv, int total, int max_seqlen, int d, int causal,
+                                    float scale, const attn_fwd_opts* opts);
 
 /* Tile shape the kernel uses for head dim d: query rows per workgroup and keys
  * per KV tile (the granularity of the online softmax and of the rescale

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(bnd.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.attn_abi_version() == bnd.ABI_VERSION == 2
+    assert lib.attn_abi_version() == bnd.ABI_VERSION == 3
 
 
 def check(*args, **kw):
@@ -174,3 +174,51 @@ def test_gqa_same_codes_as_mha_when_heads_equal():
     for a in cases:
         g = a[:6] + (a[6],) + a[6:]
         assert check(*a) == gqa_check(*g) != bnd.ATTN_OK
+
+
+CU = 6 * GB
+
+
+def varlen_check(*args, **kw):
+    return bnd.attn_fwd_varlen_check(*args, **kw)
+
+
+def test_varlen_valid_arguments_pass():
+    # (q, k, v, o, lse, cu, B, H, Hkv, total, max_seqlen, d, causal, scale)
+    assert varlen_check(Q, K, V, O, L, CU, 24, 32, 8, 42747, 5753, 128, 1, 0.088) == bnd.ATTN_OK
+    assert varlen_check(Q, K, V, O, L, CU, 3, 4, 4, 100, 1000, 64, 0, 1.0) == bnd.ATTN_OK  # max > total
+    for empty in [(0, 4, 2, 100, 50), (3, 0, 0, 100, 50), (3, 4, 2, 0, 0), (3, 4, 2, 100, 0)]:
+        B, H, Hkv, T, mx = empty
+        assert varlen_check(None, None, None, None, None, None, B, H, Hkv, T, mx, 64, 1, 1.0) == bnd.ATTN_OK
+        assert bnd.attn_fwd_varlen(None, None, None, None, None, None, B, H, Hkv, T, mx, 64, 1, 1.0,
+                                   None, None) == bnd.ATTN_OK
+
+
+@pytest.mark.parametrize("args,code", [
+    ((Q, K, V, O, L, None, 2, 4, 2, 64, 32, 64, 0, 1.0), 1),      # cu_seqlens NULL
+    ((Q, K, V, O, L, CU, -1, 4, 2, 64, 32, 64, 0, 1.0), 2),
+    ((Q, K, V, O, L, CU, 2, 4, 2, -64, 32, 64, 0, 1.0), 2),
+    ((Q, K, V, O, L, CU, 2, 4, 2, 64, -1, 64, 0, 1.0), 2),
+    ((Q, K, V, O, L, CU, 2, 4, 3, 64, 32, 64, 0, 1.0), 2),        # Hkv does not divide H
+    ((Q, K, V, O, L, CU, 2, 4, 2, 1 << 23, 32, 128, 0, 1.0), 2),  # token axis past 32-bit offsets
+    ((Q, K, V, O, L, CU, 2, 4, 2, 64, 32, 96, 0, 1.0), 3),
+    ((Q, K, V, O, L, CU + 2, 2, 4, 2, 64, 32, 64, 0, 1.0), 4),
+    ((Q, K, V, O, L, CU, 2, 4, 2, 64, 32, 64, 0, math.nan), 5),
+    ((Q, K, V, CU - 64, L, CU, 2, 4, 2, 64, 32, 64, 0, 1.0), 6),   # o overlaps cu_seqlens
+    ((Q, K, V, O, CU - 4, CU, 2, 4, 2, 64, 32, 64, 0, 1.0), 6),    # lse overlaps cu_seqlens
+    ((Q, K, V, O, K + 64, CU, 2, 4, 2, 64, 32, 64, 0, 1.0), 6),
+])
+def test_varlen_error_codes(args, code):
+    assert varlen_check(*args) == code
+    assert bnd.last_error() != ""
+    assert bnd.attn_fwd_varlen(*args, None, None) == code
+
+
+def test_varlen_alias_uses_packed_extents():
+    """q spans H*total*d elements, k and v Hkv*total*d, lse H*total floats."""
+    H, Hkv, T, d = 4, 2, 100, 64
+    kv_bytes = Hkv * T * d * 2
+    assert varlen_check(Q, K, V, K + kv_bytes, L, CU, 3, H, Hkv, T, 50, d, 0, 1.0) == bnd.ATTN_OK
+    assert varlen_check(Q, K, V, K + kv_bytes - 16, L, CU, 3, H, Hkv, T, 50, d, 0, 1.0) == 6
+    assert varlen_check(Q, K, V, O, O + H * T * d * 2, CU, 3, H, Hkv, T, 50, d, 0, 1.0) == bnd.ATTN_OK
+    assert varlen_check(Q, K, V, O, O + H * T * d * 2 - 4, CU, 3, H, Hkv, T, 50, d, 0, 1.0) == 6
