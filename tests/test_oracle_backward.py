@@ -1,0 +1,150 @@
+"""The backward oracle against what the mathematics fixes (CPU only).
+
+The backward pass is the derivative of the forward definition ([JG] "Online
+softmax and recomputation": the training pass recomputes the attention matrix
+instead of storing it). Pins: central finite differences of L = sum(O * dO)
+through the (separately pinned) forward oracle; torch autograd in float64 on
+the plain formula; closed-form identities; and planted slips that the
+finite-difference pin must catch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.backward as ob
+from exact_attention_22_amd import inputs
+
+
+def fd_gradients(q, k, v, do, causal, scale, eps=1e-6):
+    """Central differences of L = sum(O * dO) w.r.t. every element of q, k and v."""
+    q, k, v, do = (np.array(t, dtype=np.float64) for t in (q, k, v, do))
+
+    def loss():
+        return float((oracle.attention_gqa(q, k, v, causal, scale)[0] * do).sum())
+
+    grads = []
+    for x in (q, k, v):
+        g = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = loss()
+            x[idx] = keep - eps
+            lm = loss()
+            x[idx] = keep
+            g[idx] = (lp - lm) / (2 * eps)
+        grads.append(g)
+    return grads
+
+
+def _draw(B, H, Hkv, N, d, seed):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((B, H, N, d)), r.standard_normal((B, Hkv, N, d)),
+            r.standard_normal((B, Hkv, N, d)), r.standard_normal((B, H, N, d)))
+
+
+SHAPES = [(1, 1, 1, 4, 3), (1, 2, 1, 3, 2), (2, 2, 2, 3, 2), (1, 4, 2, 3, 2)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_finite_differences(shape, causal):
+    q, k, v, do = _draw(*shape, seed=sum(shape) + causal)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, causal, 0.6)
+    fq, fk, fv = fd_gradients(q, k, v, do, causal, 0.6)
+    for a, b in ((dq, fq), (dk, fk), (dv, fv)):
+        assert np.max(np.abs(a - b)) <= 1e-7
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_torch_autograd_float64(causal):
+    B, H, Hkv, N, d = 2, 4, 2, 9, 5
+    q, k, v, do = _draw(B, H, Hkv, N, d, seed=11 + causal)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    G = H // Hkv
+    kk, vv = tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1)
+    s = 0.3 * torch.matmul(tq, kk.transpose(-1, -2))
+    if causal:
+        s = s.masked_fill(~torch.tril(torch.ones(N, N, dtype=torch.bool)), float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), vv)
+    (o * torch.tensor(do)).sum().backward()
+    dq, dk, dv, dd = oracle.attention_backward(q, k, v, do, causal, 0.3)
+    assert np.max(np.abs(dq - tq.grad.numpy())) <= 1e-12
+    assert np.max(np.abs(dk - tk.grad.numpy())) <= 1e-12
+    assert np.max(np.abs(dv - tv.grad.numpy())) <= 1e-12
+    assert np.max(np.abs(dd - (o.detach().numpy() * do).sum(-1))) <= 1e-12
+
+
+def test_identities():
+    """Rows of P sum to one and dS rows sum to zero, so sum_j dK_j = 0 and
+    sum_j dV_j = sum_i dO_i (per key/value head, over its query heads); causal row 0
+    sees one key, so dQ_0 = 0; D_i = dO_i . O_i."""
+    q, k, v, do = inputs.draw(2, 4, 33, 8, seed=12) + (inputs.draw(2, 4, 33, 8, seed=13)[0],)
+    for causal in (False, True):
+        dq, dk, dv, dd = oracle.attention_backward(q, k, v, do, causal, 0.35)
+        dof = do.double().numpy()
+        assert np.max(np.abs(dk.sum(axis=2))) <= 1e-12
+        assert np.max(np.abs(dv.sum(axis=2) - dof.sum(axis=2))) <= 1e-12
+        o, _ = oracle.attention(q, k, v, causal, 0.35)
+        assert np.max(np.abs(dd - (o * dof).sum(-1))) <= 1e-12
+        if causal:
+            assert np.max(np.abs(dq[:, :, 0])) == 0.0
+
+
+def test_sampled_rows_match_full():
+    B, H, Hkv, N, d = 1, 4, 2, 40, 8
+    q, k, v = inputs.draw_gqa(B, H, Hkv, N, d, seed=14)
+    do = inputs.draw(B, H, N, d, seed=15)[0]
+    for causal in (False, True):
+        dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, causal, 0.3)
+        pq = [(0, 3, [0, 17, 39]), (0, 0, [5, 6])]
+        pkv = [(0, 1, [0, 38, 39]), (0, 0, [20])]
+        rq, rkv = oracle.attention_backward_rows(q, k, v, do, causal, 0.3, pq, pkv)
+        for (b, h, rows), x in zip(pq, rq):
+            assert np.max(np.abs(x - dq[b, h, rows])) <= 1e-13
+        for (b, g, rows), (xk, xv) in zip(pkv, rkv):
+            assert np.max(np.abs(xk - dk[b, g, rows])) <= 1e-13
+            assert np.max(np.abs(xv - dv[b, g, rows])) <= 1e-13
+
+
+def _mutant(slip):
+    def head(qh, kh, vh, doh, causal, scale):
+        n = qh.shape[0]
+        s = scale * (qh @ kh.T)
+        if causal:
+            s = np.where(np.tril(np.ones((n, n), dtype=bool)), s, -np.inf)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        dv = (p @ doh) if slip == "dv_not_transposed" else p.T @ doh
+        dp = doh @ vh.T
+        dd = dp.sum(axis=1) if slip == "d_without_p" else (p * dp).sum(axis=1)
+        ds = p * dp if slip == "no_d_term" else p * (dp - dd[:, None])
+        dq = (ds @ kh) if slip == "dq_no_scale" else scale * (ds @ kh)
+        dk = scale * (ds @ qh) if slip == "dk_not_transposed" else scale * (ds.T @ qh)
+        if slip == "dk_from_keys":
+            dk = scale * (ds.T @ kh)
+        return dq, dk, dv, dd
+    return head
+
+
+@pytest.mark.parametrize("slip", ["dv_not_transposed", "d_without_p", "no_d_term", "dq_no_scale",
+                                  "dk_not_transposed", "dk_from_keys"])
+def test_planted_slip_is_caught(monkeypatch, slip):
+    monkeypatch.setattr(ob, "_head_backward", _mutant(slip))
+    caught = False
+    for shape in SHAPES[:3]:
+        for causal in (False, True):
+            q, k, v, do = _draw(*shape, seed=40 + causal)
+            dq, dk, dv, _ = ob.attention_backward(q, k, v, do, causal, 0.6)
+            fq, fk, fv = fd_gradients(q, k, v, do, causal, 0.6)
+            caught |= any(np.max(np.abs(a - b)) > 1e-7 for a, b in ((dq, fq), (dk, fk), (dv, fv)))
+    assert caught
+
+
+def test_unmutated_copy_passes(monkeypatch):
+    monkeypatch.setattr(ob, "_head_backward", _mutant(None))
+    q, k, v, do = _draw(1, 2, 1, 3, 2, seed=41)
+    dq, dk, dv, _ = ob.attention_backward(q, k, v, do, True, 0.6)
+    fq, fk, fv = fd_gradients(q, k, v, do, True, 0.6)
+    assert all(np.max(np.abs(a - b)) <= 1e-7 for a, b in ((dq, fq), (dk, fk), (dv, fv)))
