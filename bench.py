@@ -125,6 +125,39 @@ def time_workload(w, steps, warmup, **kw):
     return ms
 
 
+def time_backward(w, steps, warmup):
+    """Average time (ms) of one attn_bwd call (dq and dk/dv kernels) on a dense
+    workload's shape, with O and LSE from one forward pass; dO drawn N(0,1)."""
+    import torch
+
+    from exact_attention_22_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inputs.workload_inputs(w))
+    do = inputs.draw(w.B, w.H, w.N, w.d, seed=w.seed + 7919)[0].to(dev)
+    o, lse = binding.attention(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty_like(lse)
+
+    def call():
+        binding.attention_backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                                   delta=delta)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del q, k, v, do, o, lse, dq, dk, dv, delta
+    torch.cuda.empty_cache()
+    return ms
+
+
 def time_samples(w, n_samples=20, min_ms=50.0):
     """n_samples timed batches of back-to-back launches, each at least min_ms long;
     per-launch median and min (ms)."""
@@ -249,6 +282,15 @@ def main():
                               "frac_peak": round(ot / PEAK_BF16_TFLOPS, 4), "causal": o.causal,
                               "shape": describe(o)}
 
+    backward = {}
+    if not args.no_others:  # backward pass (2.5x the forward flops: five N^2 d products)
+        for name in ("headline", "causal2k", "long32k"):
+            o = inputs.BY_NAME[name]
+            bms = time_backward(o, max(5, args.steps // 5), 3)
+            bt = 2.5 * o.flops / (bms * 1e-3) / 1e12
+            backward[name] = {"ms": round(bms, 4), "tflops": round(bt, 1), "frac_peak": round(bt / PEAK_BF16_TFLOPS, 4),
+                              "causal": o.causal, "shape": describe(o)}
+
     line = {
         "metric": "attention fwd TFLOP/s (bf16, causal & non-causal) and % of MI355X MFMA peak",
         "value": round(tflops, 2),
@@ -272,6 +314,7 @@ def main():
         "timed_wall_s": round(wall, 2),
         "samples": samples,
         "workloads": others,
+        "backward": backward,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

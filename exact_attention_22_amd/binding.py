@@ -23,8 +23,9 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_DIM", 3: "ATTN_ERR_UNSU
 O_BF16, O_F32 = 0, 1
 EXPORTS = ["attn_fwd", "attn_fwd_ex", "attn_fwd_check", "attn_fwd_opts_init", "attn_status_str",
            "attn_last_error", "attn_abi_version", "attn_exp2_poly_host", "attn_fwd_tile_shape",
-           "attn_fwd_gqa", "attn_fwd_gqa_check", "attn_fwd_varlen", "attn_fwd_varlen_check"]
-ABI_VERSION = 3
+           "attn_fwd_gqa", "attn_fwd_gqa_check", "attn_fwd_varlen", "attn_fwd_varlen_check",
+           "attn_bwd", "attn_bwd_check"]
+ABI_VERSION = 4
 
 
 class AttnFwdOpts(ctypes.Structure):
@@ -67,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_varlen.restype = i
         L.attn_fwd_varlen_check.argtypes = varlen_args
         L.attn_fwd_varlen_check.restype = i
+        bwd_args = [vp] * 10 + [i, i, i, i, i, i, f]
+        L.attn_bwd.argtypes = bwd_args + [vp]
+        L.attn_bwd.restype = i
+        L.attn_bwd_check.argtypes = bwd_args
+        L.attn_bwd_check.restype = i
         L.attn_fwd_opts_init.argtypes = [ctypes.POINTER(AttnFwdOpts)]
         L.attn_fwd_opts_init.restype = None
         L.attn_status_str.argtypes = [i]
@@ -245,3 +251,52 @@ def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
     if st != ATTN_OK:
         raise AttnError(st, last_error())
     return (out, lse, counts) if rescale_count else (out, lse)
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, causal, scale, stream) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return lib().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, int(causal), scale, stream)
+
+
+def attn_bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, causal, scale) -> int:
+    return lib().attn_bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, int(causal), scale)
+
+
+def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                       dout: torch.Tensor, causal: bool = False, scale: float | None = None, *,
+                       dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                       dv: torch.Tensor | None = None, delta: torch.Tensor | None = None):
+    """Exact attention backward on the current stream: returns (dQ, dK, dV, delta).
+
+    q, o, dout: bfloat16 [B,H,N,d]; k, v: bfloat16 [B,Hkv,N,d]; lse: float32 [B,H,N]
+    (o and lse from the forward pass with the same causal flag and scale). delta
+    (float32 [B,H,N]) holds D_i = dout_i . o_i.
+    """
+    _check_tensor("q", q)
+    B, H, N, d = q.shape
+    _check_tensor("k", k)
+    Hkv = k.shape[1]
+    _check_tensor("k", k, (B, Hkv, N, d))
+    _check_tensor("v", v, (B, Hkv, N, d))
+    _check_tensor("o", o, (B, H, N, d))
+    _check_tensor("dout", dout, (B, H, N, d))
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+            or not lse.is_contiguous() or lse.device != q.device):
+        raise TypeError("lse must be a contiguous float32 [B,H,N] tensor on q's device")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    for name, t, shape in (("dq", dq, (B, H, N, d)), ("dk", dk, (B, Hkv, N, d)), ("dv", dv, (B, Hkv, N, d))):
+        _check_tensor(name, t, shape)
+    if delta.dtype != torch.float32 or tuple(delta.shape) != (B, H, N) or not delta.is_contiguous():
+        raise TypeError("delta must be a contiguous float32 [B,H,N] tensor")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, Hkv, N, d, causal, scale,
+                  stream)
+    if st != ATTN_OK:
+        raise AttnError(st, last_error())
+    return dq, dk, dv, delta

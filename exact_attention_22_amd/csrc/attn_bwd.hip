@@ -1,0 +1,112 @@
+// attn_bwd.hip - C ABI, argument checks and launches of the gfx950 attention
+// backward kernels (attn_bwd_kernel.h). The contract of every entry point is
+// documented in include/attn_bwd.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_bwd.h"
+#include "attn_bwd_kernel.h"
+#include "attn_host.h"
+
+namespace {
+
+using attn_host::fail;
+using attn_host::overlaps;
+
+attn_status_t validate(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                       const void* dq, const void* dk, const void* dv, const float* delta, int B, int H, int Hkv,
+                       int N, int d, float scale, bool* work) {
+  attn_host::clear_error();
+  *work = false;
+  if (B < 0 || H < 0 || N < 0) return fail(ATTN_ERR_DIM, "negative size B=%d H=%d N=%d", B, H, N);
+  if (H > 0 ? (Hkv < 1 || Hkv > H || H % Hkv != 0) : Hkv != 0)
+    return fail(ATTN_ERR_DIM, "key/value heads Hkv=%d must divide query heads H=%d", Hkv, H);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  if (!isfinite(scale)) return fail(ATTN_ERR_SCALE, "scale is not finite");
+  if ((int64_t)B * H * N == 0) return ATTN_OK;
+  const int64_t rows = (int64_t)B * H * N;
+  const int64_t tiles = (int64_t)B * H * ((N + attn_grad::kRows - 1) / attn_grad::kRows);
+  if (rows > (int64_t)1 << 40 || tiles > INT32_MAX)
+    return fail(ATTN_ERR_DIM, "problem too large: B*H*N=%lld", (long long)rows);
+  if ((int64_t)(N + 256) * d * 2 > INT32_MAX) return fail(ATTN_ERR_DIM, "N=%d too long for one head", N);
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta)
+    return fail(ATTN_ERR_NULL, "NULL tensor pointer");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk |
+       (uintptr_t)dv) & 15)
+    return fail(ATTN_ERR_MISALIGNED, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+  if (((uintptr_t)lse | (uintptr_t)delta) & 3) return fail(ATTN_ERR_MISALIGNED, "lse and delta must be 4-byte aligned");
+  const size_t qb = (size_t)rows * d * 2, kvb = (size_t)B * Hkv * N * d * 2, lb = (size_t)rows * 4;
+  const void* ins[6] = {q, k, v, o, lse, dout};
+  const size_t in_b[6] = {qb, kvb, kvb, qb, lb, qb};
+  const void* outs[4] = {dq, dk, dv, delta};
+  const size_t out_b[4] = {qb, kvb, kvb, lb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_b[i], ins[j], in_b[j])) return fail(ATTN_ERR_ALIAS, "an output overlaps an input");
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], out_b[i], outs[j], out_b[j])) return fail(ATTN_ERR_ALIAS, "two outputs overlap");
+  }
+  *work = true;
+  return ATTN_OK;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const attn_grad::BwdParams& p, int B, int Hkv, hipStream_t stream) {
+  void* args[] = {const_cast<attn_grad::BwdParams*>(&p)};
+  const dim3 block(64 * attn_grad::kWaves);
+  // dq first: it stores D, which the dkdv kernel reads (same stream, in order)
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_grad::attn_bwd_dq_kernel<D, CAUSAL>),
+                                 dim3(B * p.H * p.n_tiles), block, args, 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_grad::attn_bwd_dkdv_kernel<D, CAUSAL>),
+                         dim3(B * Hkv * p.n_tiles), block, args, 0, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, const void* dq, const void* dk, const void* dv, const float* delta,
+                             int B, int H, int Hkv, int N, int d, int causal, float scale) {
+  (void)causal;
+  bool work;
+  return validate(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, scale, &work);
+}
+
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int Hkv, int N,
+                       int d, int causal, float scale, void* stream) {
+  bool work = false;
+  const attn_status_t st = validate(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, scale, &work);
+  if (st != ATTN_OK || !work) return st;
+  attn_grad::BwdParams p;
+  p.q = (const __bf16*)q;
+  p.k = (const __bf16*)k;
+  p.v = (const __bf16*)v;
+  p.o = (const __bf16*)o;
+  p.lse = lse;
+  p.dout = (const __bf16*)dout;
+  p.dq = (__bf16*)dq;
+  p.dk = (__bf16*)dk;
+  p.dv = (__bf16*)dv;
+  p.delta = delta;
+  p.N = N;
+  p.H = H;
+  p.G = H / Hkv;
+  p.n_tiles = (N + attn_grad::kRows - 1) / attn_grad::kRows;
+  p.scale = scale;
+  p.c = scale * 1.44269504088896341f;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (d == 128)
+    e = causal ? launch<128, true>(p, B, Hkv, s) : launch<128, false>(p, B, Hkv, s);
+  else
+    e = causal ? launch<64, true>(p, B, Hkv, s) : launch<64, false>(p, B, Hkv, s);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,376 @@
+// attn_bwd_kernel.h - exact-attention backward kernels for gfx950 (MI355X).
+//
+// The backward pass recomputes the attention probabilities on chip from Q, K
+// and the stored log-sum-exp instead of reading a stored N x N matrix (page
+// "Flash Attention" glossary, section "Online softmax and recomputation"), and
+// forms the gradients without atomic additions (page "FlashAttention-4:
+// algorithm-kernel fused pipeline for asymmetric hardware scaling", section 2,
+// names shared-memory traffic and atomics as the costs of the backward pass).
+// With dO the gradient arriving at O, for one head:
+//
+//   P = exp(scale * Q K^T - LSE)   dV = P^T dO   dP = dO V^T
+//   D_i = dO_i . O_i               dS = P * (dP - D)
+//   dQ = scale * dS K              dK = scale * dS^T Q
+//
+// Two kernels, each owning its outputs (no atomics):
+//   dq kernel:   a workgroup owns 128 query rows (32 per wavefront, one per
+//                lane). It computes D for its rows (and stores it), then walks
+//                the key tiles: S^T = K Q^T and dP^T = V dO^T on the matrix
+//                cores, dS^T on the VALU, dQ^T += K^T dS^T.
+//   dkdv kernel: a workgroup owns 128 key rows of one key/value head (one per
+//                lane) and walks the query tiles of every query head that
+//                reads it: S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
+//                dK^T += Q^T dS. It reads D from the dq kernel, which runs first.
+// Both use the 32x32x16 bf16 MFMA in the layout of the forward kernel: lane l
+// holds column l % 32 of the accumulator, so the row that a lane owns needs no
+// cross-lane reduction, and the bf16 P (or dS) of one product is the B operand
+// of the next. The A operands are 16-byte row reads of an LDS tile (K, V, Q,
+// dO) or transpose reads of the same tile (ds_read_b64_tr_b16), so every LDS
+// tile uses one XOR swizzle that is free of bank conflicts for both: 16
+// consecutive rows at one 16-byte chunk, and 4 aligned rows at 4 aligned chunks.
+#ifndef ATTN_BWD_KERNEL_H
+#define ATTN_BWD_KERNEL_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn_grad {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct BwdParams {
+  const __bf16* q;    // [B][H][N][D]
+  const __bf16* k;    // [B][Hkv][N][D]
+  const __bf16* v;    // [B][Hkv][N][D]
+  const __bf16* o;    // [B][H][N][D]
+  const float* lse;   // [B][H][N], natural log
+  const __bf16* dout; // [B][H][N][D]
+  __bf16* dq;         // [B][H][N][D]
+  __bf16* dk;         // [B][Hkv][N][D]
+  __bf16* dv;         // [B][Hkv][N][D]
+  float* delta;       // [B][H][N]: D_i = dO_i . O_i (written by the dq kernel)
+  int N;
+  int H;
+  int G;              // query heads per key/value head
+  int n_tiles;        // ceil(N / 128) row tiles per head
+  float scale;
+  float c;            // scale * log2(e)
+};
+
+constexpr int kWaves = 4;            // one wavefront per SIMD
+constexpr int kRows = 32 * kWaves;   // rows a workgroup owns
+constexpr int kTile = 64;            // rows of the streamed tiles
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Chunk swizzle of LDS row r (16-byte chunks; D/8 per row).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+// 16-byte chunk c of row R (row read; A operand rows).
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const char* t, int R, int c) {
+  return *(const bf16x8*)(t + R * (2 * D) + ((c ^ swz<D>(R)) << 4));
+}
+
+// Transpose read: lane l receives column col0 + l % 32 of rows row0 + 4*(l/32) + e,
+// e = 0..3 (lane l supplies the address of row row0 + 4*(l/32) + (l%16)/4, columns
+// col0 + 16*((l/16)%2) + 4*(l%4) .. +3).
+template <int D>
+__device__ __forceinline__ s16x4 tr4(const char* t, int row0, int col0, int lane) {
+  const int r = row0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const char* a = t + r * (2 * D) + (((col >> 3) ^ swz<D>(r)) << 4) + ((col & 7) << 1);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_void*)a);
+}
+
+// A operand of a product contracting over tile rows: k-step covering rows
+// row0 .. row0+15 (lane l's eight rows: row0 + 8*(j/4) + 4*(l/32) + j%4), feature
+// block col0 .. col0+31 (lane l: feature col0 + l%32).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* t, int row0, int col0, int lane) {
+  const s16x4 lo = tr4<D>(t, row0, col0, lane);
+  const s16x4 hi = tr4<D>(t, row0 + 8, col0, lane);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Loads rows r0 .. r0+63 of a row-major [n][D] bf16 matrix at `base` into an LDS
+// tile with the swizzle; rows >= n read as zeros. Four wavefronts share the work,
+// each lane fills 16 bytes per load at tile + 1 KiB * load + 16 * lane.
+template <int D>
+__device__ __forceinline__ void load_tile64(const __bf16* base, int n, int r0, char* tile, int wave, int lane) {
+  constexpr int CH = D / 8;          // chunks per row
+  constexpr int RPL = 64 / CH;       // rows per wave-load
+  constexpr int LOADS = kTile / RPL; // wave-loads per tile
+  const uint32_t bytes = r0 < n ? (uint32_t)(n - r0) * D * 2 : 0u;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(base + (size_t)(r0 < n ? r0 : 0) * D, __builtin_amdgcn_readfirstlane(bytes));
+  static_assert(LOADS % kWaves == 0, "tile load split");
+#pragma unroll
+  for (int ii = 0; ii < LOADS / kWaves; ++ii) {
+    const int i = ii * kWaves + wave;
+    const int r = i * RPL + lane / CH;
+    const int c = (lane % CH) ^ swz<D>(r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + i * 1024), 16, (uint32_t)(r * D + 8 * c) * 2, 0,
+                                             0, 0);
+  }
+}
+
+// 64 floats at base[r0 ..] (zeros past n) into LDS, by one wavefront.
+__device__ __forceinline__ void load_vec64(const float* base, int n, int r0, float* dst, int lane) {
+  const uint32_t bytes = r0 < n ? (uint32_t)(n - r0) * 4 : 0u;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(base + (r0 < n ? r0 : 0), __builtin_amdgcn_readfirstlane(bytes));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, (uint32_t)lane * 4, 0, 0, 0);
+}
+
+// B operand rows of a lane: row `row` of a [n][D] matrix, features 16*kk + 8*hl .. +7.
+template <int D>
+__device__ __forceinline__ void load_row_operand(bf16x8 (&dst)[D / 16], const __bf16* base, int n, int row, int hl) {
+  const __amdgpu_buffer_rsrc_t rs = rsrc(base, (uint32_t)n * D * 2);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    dst[kk] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(row * D + 16 * kk + 8 * hl) * 2, 0, 0));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Stores accumulator rows: lane l owns row `row`, accumulator block mt holds
+// features 32*mt + 8*(r/4) + 4*(l/32) + r%4 in register r; multiplied by `mul`.
+template <int D>
+__device__ __forceinline__ void store_rows(__bf16* out, size_t row, const f32x16 (&acc)[D / 32], float mul, int hl) {
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[mt][4 * gq + e] * mul);
+      *(bf16x4*)(out + row * D + 32 * mt + 8 * gq + 4 * hl) = w;
+    }
+}
+
+__device__ __forceinline__ void sync_tiles() {
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's tile loads and LDS accesses are done
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// dq kernel: workgroup = (b, h, 128 query rows).
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1) attn_bwd_dq_kernel(const BwdParams p) {
+  constexpr int KK = D / 16, MT = D / 32, NC = kTile / 32;
+  constexpr int TB = kTile * D * 2;
+  __shared__ __attribute__((aligned(1024))) char kt[2][TB];
+  __shared__ __attribute__((aligned(1024))) char vt[2][TB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int N = p.N;
+  const int bh = blockIdx.x / p.n_tiles;
+  const int i0 = (blockIdx.x - bh * p.n_tiles) * kRows;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int kvh = b * (p.H / p.G) + h / p.G;
+  const size_t qhead = (size_t)bh * N * D;
+  const size_t kvhead = (size_t)kvh * N * D;
+  const int my_q = i0 + 32 * wave + l32;
+
+  bf16x8 qreg[KK], doreg[KK], oreg[KK];
+  load_row_operand<D>(qreg, p.q + qhead, N, my_q, hl);
+  load_row_operand<D>(doreg, p.dout + qhead, N, my_q, hl);
+  load_row_operand<D>(oreg, p.o + qhead, N, my_q, hl);
+  const __amdgpu_buffer_rsrc_t lrs = rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4);
+  const float lse2 =
+      __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lrs, (uint32_t)my_q * 4, 0, 0)) * 1.44269504088896341f;
+  float dpart = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart = fmaf((float)doreg[kk][e], (float)oreg[kk][e], dpart);
+  const float Di = pair_sum(dpart);
+  if (my_q < N && hl == 0) p.delta[(size_t)bh * N + my_q] = Di;
+
+  const int kv_end = CAUSAL ? min(N, i0 + kRows) : N;
+  const int n_kt = (kv_end + kTile - 1) / kTile;
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+
+  load_tile64<D>(p.k + kvhead, N, 0, kt[0], wave, lane);
+  load_tile64<D>(p.v + kvhead, N, 0, vt[0], wave, lane);
+  sync_tiles();
+  for (int t = 0; t < n_kt; ++t) {
+    const int cur = t & 1;
+    const int j0 = t * kTile;
+    if (t + 1 < n_kt) {
+      load_tile64<D>(p.k + kvhead, N, j0 + kTile, kt[cur ^ 1], wave, lane);
+      load_tile64<D>(p.v + kvhead, N, j0 + kTile, vt[cur ^ 1], wave, lane);
+    }
+    const char* K = kt[cur];
+    const char* V = vt[cur];
+    f32x16 s[NC], dp[NC];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      s[cc] = f32x16{};
+      dp[cc] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(K, 32 * cc + l32, 2 * kk + hl), qreg[kk], s[cc],
+                                                        0, 0, 0);
+        dp[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(V, 32 * cc + l32, 2 * kk + hl), doreg[kk],
+                                                         dp[cc], 0, 0, 0);
+      }
+    }
+    // dS^T in the B-operand order of the next product: k-step 2*cc + hh holds keys
+    // 32*cc + 16*hh + 8*(j/4) + 4*hl + j%4 (register r = 8*hh + j of the block).
+    const bool edge = j0 + kTile > N || (CAUSAL && j0 + kTile - 1 > i0 + 32 * wave);
+    bf16x8 dsb[NC][2];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[cc][r], p.c, -lse2));
+        if (edge) {
+          const int key = j0 + 32 * cc + 8 * (r / 4) + 4 * hl + (r % 4);
+          pr = (key >= N || (CAUSAL && key > my_q)) ? 0.f : pr;
+        }
+        dsb[cc][r / 8][r % 8] = (__bf16)(pr * (dp[cc][r] - Di));
+      }
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(K, 32 * cc + 16 * hh, 32 * mt, lane),
+                                                            dsb[cc][hh], acc[mt], 0, 0, 0);
+    sync_tiles();
+  }
+  if (my_q < N) store_rows<D>(p.dq, (size_t)bh * N + my_q, acc, p.scale, hl);
+}
+
+// ---------------------------------------------------------------------------
+// dkdv kernel: workgroup = (b, key/value head g, 128 key rows); walks the query
+// tiles of query heads g*G .. g*G + G - 1.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int KK = D / 16, MT = D / 32, NC = kTile / 32;
+  constexpr int TB = kTile * D * 2;
+  __shared__ __attribute__((aligned(1024))) char qt[2][TB];
+  __shared__ __attribute__((aligned(1024))) char dot[2][TB];
+  __shared__ __attribute__((aligned(16))) float lse_t[2][kTile];
+  __shared__ __attribute__((aligned(16))) float del_t[2][kTile];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int N = p.N;
+  const int Hkv = p.H / p.G;
+  const int bg = blockIdx.x / p.n_tiles;  // b * Hkv + g
+  const int j0w = (blockIdx.x - bg * p.n_tiles) * kRows;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const size_t kvhead = (size_t)bg * N * D;
+  const int my_k = j0w + 32 * wave + l32;
+
+  bf16x8 kreg[KK], vreg[KK];
+  load_row_operand<D>(kreg, p.k + kvhead, N, my_k, hl);
+  load_row_operand<D>(vreg, p.v + kvhead, N, my_k, hl);
+
+  f32x16 dka[MT], dva[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    dka[mt] = f32x16{};
+    dva[mt] = f32x16{};
+  }
+  // query tiles: causal rows below the workgroup's first key see none of its keys
+  const int it0 = CAUSAL ? j0w / kTile : 0;
+  const int n_qt = (N + kTile - 1) / kTile;
+  const int per_head = n_qt - it0;
+  const int steps = per_head * p.G;
+  auto issue = [&](int step, int buf) {
+    const int hq = g * p.G + step / per_head;
+    const int iq0 = (it0 + step % per_head) * kTile;
+    const size_t qhead = ((size_t)b * p.H + hq) * N;
+    load_tile64<D>(p.q + qhead * D, N, iq0, qt[buf], wave, lane);
+    load_tile64<D>(p.dout + qhead * D, N, iq0, dot[buf], wave, lane);
+    if (wave == 0) load_vec64(p.lse + qhead, N, iq0, lse_t[buf], lane);
+    if (wave == 1) load_vec64(p.delta + qhead, N, iq0, del_t[buf], lane);
+  };
+  if (steps > 0) issue(0, 0);
+  sync_tiles();
+  for (int t = 0; t < steps; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < steps) issue(t + 1, cur ^ 1);
+    const int iq0 = (it0 + t % per_head) * kTile;
+    const char* Q = qt[cur];
+    const char* dO = dot[cur];
+    f32x16 s[NC], dp[NC];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      s[cc] = f32x16{};
+      dp[cc] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Q, 32 * cc + l32, 2 * kk + hl), kreg[kk], s[cc],
+                                                        0, 0, 0);
+        dp[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dO, 32 * cc + l32, 2 * kk + hl), vreg[kk],
+                                                         dp[cc], 0, 0, 0);
+      }
+    }
+    // Lane l holds key my_k (column) and, in register r of block cc, query row
+    // 32*cc + 8*(r/4) + 4*hl + r%4 of the tile.
+    const bool edge = iq0 + kTile > N || (CAUSAL && iq0 < j0w + 32 * wave + 32);
+    bf16x8 pb[NC][2], dsb[NC][2];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int qr = 32 * cc + 8 * gq + 4 * hl;
+        const f32x4 l4 = *(const f32x4*)&lse_t[cur][qr];
+        const f32x4 d4 = *(const f32x4*)&del_t[cur][qr];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * gq + e;
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[cc][r], p.c, -l4[e] * 1.44269504088896341f));
+          if (edge) {
+            const int qi = iq0 + qr + e;
+            pr = (qi >= N || (CAUSAL && my_k > qi)) ? 0.f : pr;
+          }
+          pb[cc][r / 8][r % 8] = (__bf16)pr;
+          dsb[cc][r / 8][r % 8] = (__bf16)(pr * (dp[cc][r] - d4[e]));
+        }
+      }
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          dva[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(dO, 32 * cc + 16 * hh, 32 * mt, lane),
+                                                            pb[cc][hh], dva[mt], 0, 0, 0);
+          dka[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(Q, 32 * cc + 16 * hh, 32 * mt, lane),
+                                                            dsb[cc][hh], dka[mt], 0, 0, 0);
+        }
+    sync_tiles();
+  }
+  if (my_k < N) {
+    store_rows<D>(p.dk, (size_t)bg * N + my_k, dka, p.scale, hl);
+    store_rows<D>(p.dv, (size_t)bg * N + my_k, dva, 1.f, hl);
+  }
+}
+
+}  // namespace attn_grad
+
+#endif

@@ -15,14 +15,16 @@
 #include <string.h>
 
 #include "attn_fwd.h"
+#include "attn_host.h"
 #include "attn_fwd_kernel.h"
 #include "exp2_poly.h"
 
-namespace {
+namespace attn_host {
 
 thread_local char g_last_error[256] = "";
 
-attn_status_t fail(attn_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error() { g_last_error[0] = '\0'; }
+
 attn_status_t fail(attn_status_t s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -35,6 +37,14 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
 }
+
+}  // namespace attn_host
+
+namespace {
+
+using attn_host::fail;
+using attn_host::g_last_error;
+using attn_host::overlaps;
 
 // Tile configuration: 8 wavefronts (256 query rows) per workgroup, BC keys per KV tile.
 constexpr int kWaves = 8;

@@ -1,0 +1,68 @@
+/*
+ * attn_bwd.h - C ABI of the MI355X (gfx950) exact-attention backward pass.
+ *
+ * Operation: the gradients of the exact attention of attn_fwd.h with respect
+ * to q, k and v, given dO, the gradient arriving at its output O. The
+ * attention probabilities are recomputed on chip from q, k and the forward
+ * pass's log-sum-exp instead of being stored (page "Flash Attention" glossary,
+ * section "Online softmax and recomputation"); the gradients are formed
+ * without atomic additions (page "FlashAttention-4: algorithm-kernel fused
+ * pipeline for asymmetric hardware scaling", section 2, on the costs of the
+ * backward pass). For batch b, query head h (key/value head g = h / (H/Hkv)),
+ * with P_ij = exp(scale * q_i . k_j - LSE_i) over the visible keys (0 otherwise):
+ *
+ *     dV[g] = sum over h in g of P^T dO          dP = dO V^T
+ *     D_i   = dO_i . O_i                          dS = P * (dP - D)
+ *     dQ    = scale * dS K                        dK[g] = sum over h in g of scale * dS^T Q
+ *
+ * Layout as in attn_fwd.h: q, o, dout, dq dense [B][H][N][d] bf16; k, v, dk,
+ * dv [B][Hkv][N][d] bf16; lse and delta [B][H][N] fp32. All DEVICE pointers.
+ * o and lse are the forward pass's outputs for the same q, k, v, causal flag
+ * and scale (any attn_fwd* entry point with bf16 O).
+ *
+ * Ownership: the caller owns every buffer; the library allocates nothing.
+ * delta is an output: D_i per query row (fp32), produced on the way and
+ * returned like dq. Every output is written in full (no accumulation into
+ * the caller's buffers).
+ *
+ * Asynchrony and errors as in attn_fwd.h: arguments are validated on the
+ * host; on success two kernels are enqueued on `stream` (dq, then dk/dv,
+ * which reads delta) and the call returns without synchronising.
+ */
+#ifndef ATTN_BWD_H
+#define ATTN_BWD_H
+
+#include "attn_fwd.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * attn_bwd - exact attention backward.
+ *   q, k, v, o, lse, dout : inputs as above (16-byte aligned; lse 4-byte).
+ *   dq, dk, dv            : bf16 outputs (16-byte aligned), fp32 accumulation,
+ *                           round-to-nearest-even on store.
+ *   delta                 : fp32 [B][H][N] output (4-byte aligned).
+ *   B, H, Hkv, N, d, causal, scale : as for attn_fwd_gqa (Hkv = H for
+ *                           multi-head attention). B*H*N == 0 returns ATTN_OK
+ *                           and launches nothing.
+ * Returns ATTN_OK; ATTN_ERR_DIM, _UNSUPPORTED, _SCALE, _NULL, _MISALIGNED as
+ * for the forward pass; ATTN_ERR_ALIAS if an output overlaps an input or
+ * another output; ATTN_ERR_HIP if a launch fails.
+ */
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
+                       int Hkv, int N, int d, int causal, float scale, void* stream);
+
+/* Host-only argument check of attn_bwd (never touches the device). */
+attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, const void* dq, const void* dk,
+                             const void* dv, const float* delta, int B, int H, int Hkv, int N,
+                             int d, int causal, float scale);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_BWD_H */

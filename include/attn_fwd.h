@@ -45,8 +45,9 @@ extern "C" {
 
 /* 1: attn_fwd, attn_fwd_ex, attn_fwd_check and helpers.
  * 2: adds attn_fwd_gqa and attn_fwd_gqa_check (grouped-query attention).
- * 3: adds attn_fwd_varlen and attn_fwd_varlen_check (packed variable-length batches). */
-#define ATTN_ABI_VERSION 3
+ * 3: adds attn_fwd_varlen and attn_fwd_varlen_check (packed variable-length batches).
+ * 4: adds attn_bwd and attn_bwd_check (backward pass, declared in attn_bwd.h). */
+#define ATTN_ABI_VERSION 4
 
 typedef enum attn_status {
   ATTN_OK = 0,

@@ -10,7 +10,8 @@ import pytest
 
 from exact_attention_22_amd import binding as bnd
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn_fwd.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = [os.path.join(INCLUDE, f) for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h")]
 
 # fake, aligned, non-overlapping device addresses: the checks never dereference them
 GB = 1 << 30
@@ -18,7 +19,7 @@ Q, K, V, O, L = 1 * GB, 2 * GB, 3 * GB, 4 * GB, 5 * GB
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
 
@@ -29,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(bnd.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.attn_abi_version() == bnd.ABI_VERSION == 3
+    assert lib.attn_abi_version() == bnd.ABI_VERSION == 4
 
 
 def check(*args, **kw):
@@ -222,3 +223,30 @@ def test_varlen_alias_uses_packed_extents():
     assert varlen_check(Q, K, V, K + kv_bytes - 16, L, CU, 3, H, Hkv, T, 50, d, 0, 1.0) == 6
     assert varlen_check(Q, K, V, O, O + H * T * d * 2, CU, 3, H, Hkv, T, 50, d, 0, 1.0) == bnd.ATTN_OK
     assert varlen_check(Q, K, V, O, O + H * T * d * 2 - 4, CU, 3, H, Hkv, T, 50, d, 0, 1.0) == 6
+
+
+DO, DQ, DK, DV, DL = 7 * GB, 8 * GB, 9 * GB, 10 * GB, 11 * GB
+
+
+def bwd_check(*args):
+    return bnd.attn_bwd_check(*args)
+
+
+def test_bwd_valid_and_empty():
+    # (q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, causal, scale)
+    assert bwd_check(Q, K, V, O, L, DO, DQ, DK, DV, DL, 2, 32, 8, 8192, 128, 1, 0.088) == bnd.ATTN_OK
+    assert bwd_check(*([None] * 10), 0, 4, 2, 16, 64, 0, 1.0) == bnd.ATTN_OK
+    assert bnd.attn_bwd(*([None] * 10), 1, 4, 2, 0, 64, 0, 1.0, None) == bnd.ATTN_OK
+
+
+@pytest.mark.parametrize("patch,code", [
+    ({0: None}, 1), ({9: None}, 1), ({12: 3}, 2), ({13: -1}, 2), ({14: 96}, 3), ({16: math.inf}, 5),
+    ({6: DQ + 8}, 4), ({9: DL + 2}, 4), ({6: Q}, 6), ({7: DQ + 64}, 6), ({9: V + 4}, 6), ({8: DK}, 6),
+])
+def test_bwd_error_codes(patch, code):
+    args = [Q, K, V, O, L, DO, DQ, DK, DV, DL, 1, 4, 2, 64, 64, 0, 1.0]
+    for i, x in patch.items():
+        args[i] = x
+    assert bwd_check(*args) == code
+    assert bnd.last_error() != ""
+    assert bnd.attn_bwd(*args, None) == code
