@@ -172,8 +172,13 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1) attn_bwd_dq_kernel(const BwdParams p) {
   constexpr int KK = D / 16, MT = D / 32, NC = kTile / 32;
   constexpr int TB = kTile * D * 2;
-  __shared__ __attribute__((aligned(1024))) char kt[2][TB];
-  __shared__ __attribute__((aligned(1024))) char vt[2][TB];
+  // Separate arrays per buffer (not one [2][TB] array): the compiler then sees that
+  // the loads into one buffer do not alias the reads of the other and does not
+  // wait for the next tile's loads before reading the current one.
+  __shared__ __attribute__((aligned(1024))) char kt0[TB];
+  __shared__ __attribute__((aligned(1024))) char kt1[TB];
+  __shared__ __attribute__((aligned(1024))) char vt0[TB];
+  __shared__ __attribute__((aligned(1024))) char vt1[TB];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -208,18 +213,15 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq_kernel(const BwdParams p) 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
 
-  load_tile64<D>(p.k + kvhead, N, 0, kt[0], wave, lane);
-  load_tile64<D>(p.v + kvhead, N, 0, vt[0], wave, lane);
+  load_tile64<D>(p.k + kvhead, N, 0, kt0, wave, lane);
+  load_tile64<D>(p.v + kvhead, N, 0, vt0, wave, lane);
   sync_tiles();
-  for (int t = 0; t < n_kt; ++t) {
-    const int cur = t & 1;
+  // Step t computes on (K, V) while tile t+1 loads into (Kn, Vn); the loads are
+  // unconditional (past the last tile they read beyond kv_end or, past N, nothing).
+  auto step = [&](int t, const char* K, const char* V, char* Kn, char* Vn) {
     const int j0 = t * kTile;
-    if (t + 1 < n_kt) {
-      load_tile64<D>(p.k + kvhead, N, j0 + kTile, kt[cur ^ 1], wave, lane);
-      load_tile64<D>(p.v + kvhead, N, j0 + kTile, vt[cur ^ 1], wave, lane);
-    }
-    const char* K = kt[cur];
-    const char* V = vt[cur];
+    load_tile64<D>(p.k + kvhead, N, j0 + kTile, Kn, wave, lane);
+    load_tile64<D>(p.v + kvhead, N, j0 + kTile, Vn, wave, lane);
     f32x16 s[NC], dp[NC];
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
@@ -257,7 +259,13 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq_kernel(const BwdParams p) 
           acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(K, 32 * cc + 16 * hh, 32 * mt, lane),
                                                             dsb[cc][hh], acc[mt], 0, 0, 0);
     sync_tiles();
+  };
+  int t = 0;
+  for (; t + 1 < n_kt; t += 2) {
+    step(t, kt0, vt0, kt1, vt1);
+    step(t + 1, kt1, vt1, kt0, vt0);
   }
+  if (t < n_kt) step(t, kt0, vt0, kt1, vt1);
   if (my_q < N) store_rows<D>(p.dq, (size_t)bh * N + my_q, acc, p.scale, hl);
 }
 
@@ -268,10 +276,15 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdParams p) {
   constexpr int KK = D / 16, MT = D / 32, NC = kTile / 32;
   constexpr int TB = kTile * D * 2;
-  __shared__ __attribute__((aligned(1024))) char qt[2][TB];
-  __shared__ __attribute__((aligned(1024))) char dot[2][TB];
-  __shared__ __attribute__((aligned(16))) float lse_t[2][kTile];
-  __shared__ __attribute__((aligned(16))) float del_t[2][kTile];
+  // One array per buffer, as in the dq kernel.
+  __shared__ __attribute__((aligned(1024))) char qt0[TB];
+  __shared__ __attribute__((aligned(1024))) char qt1[TB];
+  __shared__ __attribute__((aligned(1024))) char dot0[TB];
+  __shared__ __attribute__((aligned(1024))) char dot1[TB];
+  __shared__ __attribute__((aligned(16))) float lse0[kTile];
+  __shared__ __attribute__((aligned(16))) float lse1[kTile];
+  __shared__ __attribute__((aligned(16))) float del0[kTile];
+  __shared__ __attribute__((aligned(16))) float del1[kTile];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -299,23 +312,24 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdParams p
   const int n_qt = (N + kTile - 1) / kTile;
   const int per_head = n_qt - it0;
   const int steps = per_head * p.G;
-  auto issue = [&](int step, int buf) {
-    const int hq = g * p.G + step / per_head;
-    const int iq0 = (it0 + step % per_head) * kTile;
+  // Loads of step `st` (query head g*G + st/per_head, query tile it0 + st%per_head);
+  // a step past the last reloads the last tile, so every step issues the same loads.
+  auto issue = [&](int st, char* Qb, char* dOb, float* lb, float* db) {
+    st = min(st, steps - 1);
+    const int hq = g * p.G + st / per_head;
+    const int iq0 = (it0 + st % per_head) * kTile;
     const size_t qhead = ((size_t)b * p.H + hq) * N;
-    load_tile64<D>(p.q + qhead * D, N, iq0, qt[buf], wave, lane);
-    load_tile64<D>(p.dout + qhead * D, N, iq0, dot[buf], wave, lane);
-    if (wave == 0) load_vec64(p.lse + qhead, N, iq0, lse_t[buf], lane);
-    if (wave == 1) load_vec64(p.delta + qhead, N, iq0, del_t[buf], lane);
+    load_tile64<D>(p.q + qhead * D, N, iq0, Qb, wave, lane);
+    load_tile64<D>(p.dout + qhead * D, N, iq0, dOb, wave, lane);
+    if (wave == 0) load_vec64(p.lse + qhead, N, iq0, lb, lane);
+    if (wave == 1) load_vec64(p.delta + qhead, N, iq0, db, lane);
   };
-  if (steps > 0) issue(0, 0);
+  issue(0, qt0, dot0, lse0, del0);
   sync_tiles();
-  for (int t = 0; t < steps; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < steps) issue(t + 1, cur ^ 1);
+  auto step = [&](int t, const char* Q, const char* dO, const float* lt, const float* dt, char* Qn, char* dOn,
+                  float* ln, float* dn) {
+    issue(t + 1, Qn, dOn, ln, dn);
     const int iq0 = (it0 + t % per_head) * kTile;
-    const char* Q = qt[cur];
-    const char* dO = dot[cur];
     f32x16 s[NC], dp[NC];
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
@@ -338,8 +352,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdParams p
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int qr = 32 * cc + 8 * gq + 4 * hl;
-        const f32x4 l4 = *(const f32x4*)&lse_t[cur][qr];
-        const f32x4 d4 = *(const f32x4*)&del_t[cur][qr];
+        const f32x4 l4 = *(const f32x4*)&lt[qr];
+        const f32x4 d4 = *(const f32x4*)&dt[qr];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * gq + e;
@@ -364,7 +378,13 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdParams p
                                                             dsb[cc][hh], dka[mt], 0, 0, 0);
         }
     sync_tiles();
+  };
+  int t = 0;
+  for (; t + 1 < steps; t += 2) {
+    step(t, qt0, dot0, lse0, del0, qt1, dot1, lse1, del1);
+    step(t + 1, qt1, dot1, lse1, del1, qt0, dot0, lse0, del0);
   }
+  if (t < steps) step(t, qt0, dot0, lse0, del0, qt1, dot1, lse1, del1);
   if (my_k < N) {
     store_rows<D>(p.dk, (size_t)bg * N + my_k, dka, p.scale, hl);
     store_rows<D>(p.dv, (size_t)bg * N + my_k, dva, 1.f, hl);
