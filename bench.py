@@ -158,6 +158,37 @@ def time_backward(w, steps, warmup):
     return ms
 
 
+def time_split(w, steps, warmup):
+    """Average time (ms) of attn_fwd_splitkv (automatic split count, partial and merge
+    kernels) on a dense workload, workspace allocated once beforehand."""
+    import torch
+
+    from exact_attention_22_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inputs.workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(binding.splitkv_workspace_size(w.B, w.H, w.N, w.d, 0), dtype=torch.uint8, device=dev)
+
+    def call():
+        binding.attention_splitkv(q, k, v, causal=w.causal, scale=w.scale, n_splits=0, out=o, lse=lse, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return ms
+
+
 def time_samples(w, n_samples=20, min_ms=50.0):
     """n_samples timed batches of back-to-back launches, each at least min_ms long;
     per-launch median and min (ms)."""
@@ -291,6 +322,17 @@ def main():
             backward[name] = {"ms": round(bms, 4), "tflops": round(bt, 1), "frac_peak": round(bt / PEAK_BF16_TFLOPS, 4),
                               "causal": o.causal, "shape": describe(o)}
 
+    splitkv = {}
+    if not args.no_others:  # split keys on shapes with fewer query tiles than compute units
+        for (B, H, N, d, causal) in ((1, 2, 16384, 128, False), (1, 4, 32768, 128, True)):
+            sw = inputs.Workload(f"lowocc_{N}", B, H, N, d, causal, False, 1100 + H)
+            plain = time_workload(sw, 10, 3)
+            split = time_split(sw, 10, 3)
+            splitkv[sw.name] = {"shape": describe(sw), "causal": causal, "ms_plain": round(plain, 4),
+                                "ms_split": round(split, 4),
+                                "tflops_plain": round(sw.flops / (plain * 1e-3) / 1e12, 1),
+                                "tflops_split": round(sw.flops / (split * 1e-3) / 1e12, 1)}
+
     line = {
         "metric": "attention fwd TFLOP/s (bf16, causal & non-causal) and % of MI355X MFMA peak",
         "value": round(tflops, 2),
@@ -315,6 +357,7 @@ def main():
         "samples": samples,
         "workloads": others,
         "backward": backward,
+        "splitkv": splitkv,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -24,8 +24,8 @@ O_BF16, O_F32 = 0, 1
 EXPORTS = ["attn_fwd", "attn_fwd_ex", "attn_fwd_check", "attn_fwd_opts_init", "attn_status_str",
            "attn_last_error", "attn_abi_version", "attn_exp2_poly_host", "attn_fwd_tile_shape",
            "attn_fwd_gqa", "attn_fwd_gqa_check", "attn_fwd_varlen", "attn_fwd_varlen_check",
-           "attn_bwd", "attn_bwd_check"]
-ABI_VERSION = 4
+           "attn_bwd", "attn_bwd_check", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size"]
+ABI_VERSION = 5
 
 
 class AttnFwdOpts(ctypes.Structure):
@@ -68,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_varlen.restype = i
         L.attn_fwd_varlen_check.argtypes = varlen_args
         L.attn_fwd_varlen_check.restype = i
+        L.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t,
+                                       ctypes.POINTER(AttnFwdOpts), vp]
+        L.attn_fwd_splitkv.restype = i
+        L.attn_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
+        L.attn_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
         bwd_args = [vp] * 10 + [i, i, i, i, i, i, f]
         L.attn_bwd.argtypes = bwd_args + [vp]
         L.attn_bwd.restype = i
@@ -300,3 +305,42 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: tor
     if st != ATTN_OK:
         raise AttnError(st, last_error())
     return dq, dk, dv, delta
+
+
+def splitkv_workspace_size(B: int, H: int, N: int, d: int, n_splits: int = 0) -> int:
+    return int(lib().attn_fwd_splitkv_workspace_size(B, H, N, d, n_splits))
+
+
+def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                      scale: float | None = None, n_splits: int = 0, *, tau: float = 8.0,
+                      out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                      lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Exact attention with split keys (n_splits units per query tile, 0 = automatic),
+    merged by log-sum-exp weights. Same shapes and results (up to rounding) as
+    `attention`. `workspace`: a uint8 device tensor of at least
+    splitkv_workspace_size(...) bytes (allocated here when not given)."""
+    _check_tensor("q", q)
+    B, H, N, d = q.shape
+    _check_tensor("k", k)
+    Hkv = k.shape[1]
+    _check_tensor("k", k, (B, Hkv, N, d))
+    _check_tensor("v", v, (B, Hkv, N, d))
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    need = splitkv_workspace_size(B, H, N, d, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    opts = make_opts(tau, 0, O_F32 if out_dtype == torch.float32 else O_BF16, None)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib().attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                                Hkv, N, d, int(causal), scale, n_splits, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), ctypes.byref(opts), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, last_error())
+    return out, lse

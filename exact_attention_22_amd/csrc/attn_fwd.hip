@@ -108,6 +108,26 @@ hipError_t launch_d(const attn::Params& p, bool causal, bool of32, int poly8, bo
               : launch_poly<D, false, false>(p, poly8, neg, varlen, s);
 }
 
+// Split keys: the partial kernel (fp32 partial O and LSE per unit into the
+// workspace), then the merge kernel, on one stream.
+template <int D, bool CAUSAL>
+hipError_t launch_split(const attn::Params& p, bool neg, bool of32, int rows_total, hipStream_t stream) {
+  int per_wg_xcd = p.per_xcd;
+  const int slots = cus_per_xcd();
+  if (slots > 0 && slots < per_wg_xcd) per_wg_xcd = slots;
+  void* args[] = {const_cast<attn::Params*>(&p)};
+  const void* fn =
+      neg ? reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, true, 0, true, false, true>)
+          : reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, true, 0, false, false, true>);
+  hipError_t e = hipLaunchKernel(fn, dim3(per_wg_xcd * 8), dim3(64 * kWaves), args, 0, stream);
+  if (e != hipSuccess) return e;
+  int split_keys = p.split_tiles * Cfg<D>::BC;
+  void* margs[] = {const_cast<attn::Params*>(&p), &rows_total, &split_keys};
+  const void* mfn = of32 ? reinterpret_cast<const void*>(&attn::attn_merge_kernel<D, CAUSAL, true>)
+                         : reinterpret_cast<const void*>(&attn::attn_merge_kernel<D, CAUSAL, false>);
+  return hipLaunchKernel(mfn, dim3((rows_total + 3) / 4), dim3(256), margs, 0, stream);
+}
+
 // One call, dense ([B][H][N][d]) or packed (varlen: [H][total][d] with cu_seqlens).
 struct Problem {
   const void *q, *k, *v;
@@ -218,6 +238,11 @@ attn_status_t run(const Problem& P, int causal, const attn_fwd_opts* opts, void*
   p.c = P.scale * 1.44269504088896341f;
   if (p.c == 0.f) p.c = 0x1p-100f;
   p.tau = o2.rescale_tau_log2;
+  p.n_splits = 1;
+  p.split_tiles = 0;
+  p.ws_o = nullptr;
+  p.ws_lse = nullptr;
+  p.split_stride = 0;
 
   const bool of32 = o2.o_dtype == ATTN_O_F32;
   const bool neg = P.scale < 0.f;
@@ -225,6 +250,93 @@ attn_status_t run(const Problem& P, int causal, const attn_fwd_opts* opts, void*
       P.d == 128 ? launch_d<128>(p, causal != 0, of32, o2.exp2_poly_eighths, neg, P.varlen, (hipStream_t)stream)
                  : launch_d<64>(p, causal != 0, of32, o2.exp2_poly_eighths, neg, P.varlen, (hipStream_t)stream);
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+  return ATTN_OK;
+}
+
+// Split keys into n_splits units per query tile (0: enough units to give every
+// compute unit one). Returns the unit count through *splits and the key tiles per
+// unit through *split_tiles.
+void split_shape(int B, int H, int N, int d, int n_splits, int* splits, int* split_tiles) {
+  const int bc = d == 128 ? Cfg<128>::BC : Cfg<64>::BC;
+  const int key_tiles = (N + bc - 1) / bc;
+  int s = n_splits;
+  if (s <= 0) {
+    const int64_t units = (int64_t)B * H * ((N + kRows - 1) / kRows);
+    const int cus = cus_per_xcd() > 0 ? cus_per_xcd() * 8 : 256;
+    s = units >= cus ? 1 : (int)((cus + units - 1) / units);
+  }
+  s = s < 1 ? 1 : (s > key_tiles ? key_tiles : s);
+  const int st = (key_tiles + s - 1) / s;
+  *split_tiles = st;
+  *splits = (key_tiles + st - 1) / st;  // no unit without key tiles
+}
+
+size_t split_workspace_bytes(int B, int H, int N, int d, int splits) {
+  const size_t rows = (size_t)B * H * N;
+  const size_t o_bytes = (splits * rows * d * 4 + 255) / 256 * 256;
+  return o_bytes + splits * rows * 4;
+}
+
+attn_status_t run_split(const Problem& P, int causal, int n_splits, void* ws, size_t ws_bytes,
+                        const attn_fwd_opts* opts, void* stream) {
+  attn_fwd_opts o2;
+  bool work = false;
+  attn_status_t st = validate(P, opts, &o2, &work);
+  if (st != ATTN_OK || !work) return st;
+  if (n_splits < 0 || n_splits > 1024) return fail(ATTN_ERR_DIM, "n_splits %d outside [0, 1024]", n_splits);
+  if (o2.exp2_poly_eighths != 0) return fail(ATTN_ERR_UNSUPPORTED, "split keys: exp2_poly_eighths must be 0");
+  if (o2.rescale_count) return fail(ATTN_ERR_UNSUPPORTED, "split keys: no rescale counter");
+  int splits, split_tiles;
+  split_shape(P.B, P.H, P.N, P.d, n_splits, &splits, &split_tiles);
+  const size_t need = split_workspace_bytes(P.B, P.H, P.N, P.d, splits);
+  if (!ws) return fail(ATTN_ERR_NULL, "NULL workspace");
+  // one unit per query tile: the merge would multiply by exp(0) = 1, so the plain
+  // kernel gives the same bits without the workspace round trip
+  if (splits == 1) return run(P, causal, opts, stream);
+  if ((uintptr_t)ws & 255) return fail(ATTN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(ATTN_ERR_DIM, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  const int64_t rows = (int64_t)P.B * P.H * P.N;
+  const int64_t units = (int64_t)P.B * P.H * ((P.N + kRows - 1) / kRows) * splits;
+  if (units + 8 > INT32_MAX || rows + 4 > INT32_MAX) return fail(ATTN_ERR_DIM, "too many split units or rows");
+  const size_t q_bytes = (size_t)rows * P.d * 2, kv_bytes = (size_t)rows / P.H * P.Hkv * P.d * 2;
+  const size_t o_bytes = (size_t)rows * P.d * (o2.o_dtype == ATTN_O_F32 ? 4 : 2);
+  const void* others[5] = {P.q, P.k, P.v, P.o, P.lse};
+  const size_t other_bytes[5] = {q_bytes, kv_bytes, kv_bytes, o_bytes, (size_t)rows * 4};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(ws, need, others[i], other_bytes[i])) return fail(ATTN_ERR_ALIAS, "workspace overlaps a tensor");
+
+  attn::Params p;
+  p.q = (const __bf16*)P.q;
+  p.k = (const __bf16*)P.k;
+  p.v = (const __bf16*)P.v;
+  p.o = P.o;
+  p.lse = P.lse;
+  p.rescale_count = nullptr;
+  p.cu_seqlens = nullptr;
+  p.nseq = 0;
+  p.N = P.N;
+  p.H = P.H;
+  p.G = P.H / P.Hkv;
+  p.nq_tiles = (P.N + kRows - 1) / kRows;
+  p.total_tiles = (int)units;
+  p.per_xcd = (p.total_tiles + 7) / 8;
+  p.c = P.scale * 1.44269504088896341f;
+  if (p.c == 0.f) p.c = 0x1p-100f;
+  p.tau = o2.rescale_tau_log2;
+  p.n_splits = splits;
+  p.split_tiles = split_tiles;
+  p.ws_o = (float*)ws;
+  p.ws_lse = (float*)((char*)ws + (splits * (size_t)rows * P.d * 4 + 255) / 256 * 256);
+  p.split_stride = (size_t)rows;
+  const bool of32 = o2.o_dtype == ATTN_O_F32;
+  const bool neg = P.scale < 0.f;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (P.d == 128)
+    e = causal ? launch_split<128, true>(p, neg, of32, (int)rows, s) : launch_split<128, false>(p, neg, of32, (int)rows, s);
+  else
+    e = causal ? launch_split<64, true>(p, neg, of32, (int)rows, s) : launch_split<64, false>(p, neg, of32, (int)rows, s);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ATTN_OK;
 }
 
@@ -288,6 +400,20 @@ attn_status_t attn_fwd_gqa(const void* q, const void* k, const void* v, void* o,
                            int Hkv, int N, int d, int causal, float scale, const attn_fwd_opts* opts,
                            void* stream) {
   return run(dense(q, k, v, o, lse, B, H, Hkv, N, d, scale), causal, opts, stream);
+}
+
+size_t attn_fwd_splitkv_workspace_size(int B, int H, int N, int d, int n_splits) {
+  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128) || n_splits < 0 || n_splits > 1024) return 0;
+  int splits, split_tiles;
+  split_shape(B, H, N, d, n_splits, &splits, &split_tiles);
+  return split_workspace_bytes(B, H, N, d, splits);
+}
+
+attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                               int Hkv, int N, int d, int causal, float scale, int n_splits, void* workspace,
+                               size_t workspace_bytes, const attn_fwd_opts* opts, void* stream) {
+  return run_split(dense(q, k, v, o, lse, B, H, Hkv, N, d, scale), causal, n_splits, workspace, workspace_bytes,
+                   opts, stream);
 }
 
 attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,

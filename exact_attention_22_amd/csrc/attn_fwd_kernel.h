@@ -91,6 +91,14 @@ struct Params {
   int per_xcd;         // ceil(total_tiles / 8): workgroups per XCD slice
   float c;             // scale * log2(e) in fp32; +-2^-100 stands in for 0 (see the launcher)
   float tau;           // rescale threshold, log2 units
+  // split keys: tile (bh, qt) is n_splits units, unit s covering key tiles
+  // [s * split_tiles, (s + 1) * split_tiles); each writes its normalised O and LSE
+  // over those keys to ws_o [n_splits][B*H*N][D] and ws_lse [n_splits][B*H*N]
+  int n_splits;
+  int split_tiles;
+  float* ws_o;
+  float* ws_lse;
+  size_t split_stride;  // B * H * N rows
 };
 
 // Buffer resource over `bytes` bytes at `base`: raw loads at byte offsets >= bytes
@@ -401,7 +409,8 @@ __device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 3
 // every head and attends only to itself (causal positions counted from its
 // first token). Each tile reads its sequence's bounds; the buffer resources end
 // at the sequence's last row, so no load crosses into the next sequence.
-template <int D, int BC, bool CAUSAL, bool OF32, int POLY8, bool NEG, bool VARLEN>
+// SPLIT: split keys (see Params); requires OF32 (the partial results are fp32).
+template <int D, int BC, bool CAUSAL, bool OF32, int POLY8, bool NEG, bool VARLEN, bool SPLIT = false>
 __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   constexpr int NW = 8;            // wavefronts per workgroup (2 per SIMD)
   constexpr int BR = 32 * NW;      // query rows per workgroup
@@ -410,6 +419,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   constexpr int MT = D / 32;
   constexpr int TILEB = BC * D * 2;
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(!SPLIT || (OF32 && !VARLEN), "split keys: fp32 partials, dense layout");
 
   __shared__ __attribute__((aligned(1024))) char kbuf0[TILEB];
   __shared__ __attribute__((aligned(1024))) char kbuf1[TILEB];
@@ -442,6 +452,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   struct Tile {
     int bh, kvh, i0, n_tiles, t_full;  // kvh: the (batch, key/value head) that bh reads
     int n, start;  // packed batches: the sequence's length and first token (bh, kvh: heads)
+    int kb, sp;    // split keys: first key tile of the unit, and its split index
   };
   // Causal: a persistent workgroup's successive tiles alternate direction
   // through its XCD's range (round r of S slots takes position i or S-1-i). The
@@ -462,8 +473,13 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     }
     const int logical = (v & 7) * p.per_xcd + j;
     if (j >= p.per_xcd || logical >= p.total_tiles) return 0;
-    t.bh = logical / p.nq_tiles;
-    int qt = logical - t.bh * p.nq_tiles;
+    int unit = logical;
+    if (SPLIT) {  // logical = (bh * nq_tiles + qt) * n_splits + sp
+      unit = logical / p.n_splits;
+      t.sp = logical - unit * p.n_splits;
+    }
+    t.bh = unit / p.nq_tiles;
+    int qt = unit - t.bh * p.nq_tiles;
     int n = N;
     if (VARLEN) {
       const int h = t.bh / p.nseq, b = t.bh - h * p.nseq;
@@ -489,13 +505,19 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     t.n_tiles = (kv_end + BC - 1) / BC;
     t.t_full = n / BC;
     if (CAUSAL) t.t_full = min(t.t_full, (t.i0 + 1) / BC);
+    if (SPLIT) {  // key tiles of this unit; units past the tile's last key tile are empty
+      t.kb = t.sp * p.split_tiles;
+      if (t.kb >= t.n_tiles) return -1;
+      t.n_tiles = min(p.split_tiles, t.n_tiles - t.kb);
+      t.t_full -= t.kb;
+    }
     return 1;
   };
   // The first tile at or after slot v (advancing v past empty slots).
   auto find_tile = [&](int& v, Tile& t) -> bool {
     for (;;) {
       const int r = tile_of(v, t);
-      if (!VARLEN || r >= 0) return r > 0;
+      if (!(VARLEN || SPLIT) || r >= 0) return r > 0;
       v += (int)gridDim.x;
     }
   };
@@ -504,10 +526,13 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     const size_t head = VARLEN ? ((size_t)t.bh * N + t.start) * D : (size_t)t.bh * (size_t)N * D;
     const size_t kvhead = VARLEN ? ((size_t)t.kvh * N + t.start) * D : (size_t)t.kvh * (size_t)N * D;
     const int n = VARLEN ? t.n : N;
+    // split keys: K and V start at the unit's first key tile
+    const size_t kvoff = kvhead + (SPLIT ? (size_t)t.kb * BC * D : 0);
+    const int nkv = n - (SPLIT ? t.kb * BC : 0);
     if (grp == 1) {  // n_tiles >= 1
-      load_tile<D, BC, 4>(koff, p.k + kvhead, n, 0, kbuf0, wave & 3, true);
-      load_tile<D, BC, 4>(voff, p.v + kvhead, n, 0, vbuf0, wave & 3, true);
-      load_tile<D, BC, 4>(koff, p.k + kvhead, n, BC, kbuf1, wave & 3, t.n_tiles > 1);
+      load_tile<D, BC, 4>(koff, p.k + kvoff, nkv, 0, kbuf0, wave & 3, true);
+      load_tile<D, BC, 4>(voff, p.v + kvoff, nkv, 0, vbuf0, wave & 3, true);
+      load_tile<D, BC, 4>(koff, p.k + kvoff, nkv, BC, kbuf1, wave & 3, t.n_tiles > 1);
     }
     const __amdgpu_buffer_rsrc_t qrsrc =
         buffer_rsrc(p.q + head, VARLEN ? (uint32_t)n * D * 2 : head_bytes);
@@ -533,8 +558,12 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   const int wq0 = i0 + wave * 32;
   const int my_q = wq0 + l32;
   const size_t kvhead = VARLEN ? ((size_t)tile.kvh * p.N + tile.start) * D : (size_t)tile.kvh * (size_t)N * D;
-  const __bf16* const kh = p.k + kvhead;
-  const __bf16* const vh = p.v + kvhead;
+  // split keys: K/V pointers and row count from the unit's first key tile kt0; the
+  // masks use absolute key positions ((k + kt0) * BC against N and the query row)
+  const int kt0 = SPLIT ? tile.kb : 0;
+  const int Nkv = N - kt0 * BC;
+  const __bf16* const kh = p.k + kvhead + (size_t)kt0 * BC * D;
+  const __bf16* const vh = p.v + kvhead + (size_t)kt0 * BC * D;
 
   RowState<D> st;
 #pragma unroll
@@ -557,7 +586,8 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     auto pair = [&](int k, char* kb1, char* vb0) {
       bf16x8 pb[NC][2];
       bf16x8 va[NC][2][MT];
-      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, va, vb0, voffs, k >= t_full, k * BC, N, my_q, lane, c, tau);
+      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, va, vb0, voffs, k >= t_full, (k + kt0) * BC, N, my_q, lane,
+                                               c, tau);
       phase_barrier();
       matrix_phase<D, BC>(st, s, pb, va, qreg, kb1, lane);
       phase_barrier();
@@ -575,7 +605,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     // the previous step's loads have landed.
     auto wait_prev = [] { __builtin_amdgcn_s_waitcnt(0x0F70 | LPW); };  // vmcnt(LPW)
     // Step 0: V_1 in flight.
-    load_tile<D, BC, 4>(voff, vh, N, BC, vbuf1, wave & 3, n_tiles > 1);
+    load_tile<D, BC, 4>(voff, vh, Nkv, BC, vbuf1, wave & 3, n_tiles > 1);
     wait_prev();
     phase_barrier();
     // Steps 2k+1 (loads K_{k+2}; softmax(k)) and 2k+2 (loads V_{k+2}; matrix(k)).
@@ -583,11 +613,12 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
       bf16x8 pb[NC][2];
       bf16x8 va[NC][2][MT];
       const bool live = k + 2 < n_tiles;
-      load_tile<D, BC, 4>(koff, kh, N, (k + 2) * BC, kb0, wave & 3, live);
-      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, va, vb0, voffs, k >= t_full, k * BC, N, my_q, lane, c, tau);
+      load_tile<D, BC, 4>(koff, kh, Nkv, (k + 2) * BC, kb0, wave & 3, live);
+      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, va, vb0, voffs, k >= t_full, (k + kt0) * BC, N, my_q, lane,
+                                               c, tau);
       wait_prev();
       phase_barrier();
-      load_tile<D, BC, 4>(voff, vh, N, (k + 2) * BC, vb0, wave & 3, live);
+      load_tile<D, BC, 4>(voff, vh, Nkv, (k + 2) * BC, vb0, wave & 3, live);
       matrix_phase<D, BC>(st, s, pb, va, qreg, kb1, lane);
       wait_prev();
       phase_barrier();
@@ -609,6 +640,10 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   if (more) issue_loads(next);
 
   const float l_tot = pair_sum(st.l_sum);
+  // split keys: this unit's partial result goes to its workspace slice (a row that
+  // sees none of the unit's keys stores a value the merge does not read)
+  float* const o_out = SPLIT ? p.ws_o + (size_t)tile.sp * p.split_stride * D : (float*)p.o;
+  float* const lse_out = SPLIT ? p.ws_lse + (size_t)tile.sp * p.split_stride : p.lse;
   if (my_q < N) {
     const float inv = 1.f / l_tot;
     const size_t row = row0 + my_q;
@@ -621,7 +656,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
           f32x4 w;
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[e] = st.oacc[mt][4 * gq + e] * inv;
-          *(f32x4*)((float*)p.o + row * D + dv) = w;
+          *(f32x4*)(o_out + row * D + dv) = w;
         } else {
           bf16x4 w;
 #pragma unroll
@@ -630,8 +665,8 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
         }
       }
     if (hl == 0) {
-      p.lse[row] = 0.69314718055994531f * (st.m_used + log2f(l_tot));
-      if (p.rescale_count) p.rescale_count[row] = st.n_rescale;
+      lse_out[row] = 0.69314718055994531f * (st.m_used + log2f(l_tot));
+      if (!SPLIT && p.rescale_count) p.rescale_count[row] = st.n_rescale;
     }
   }
   if (!more) break;
@@ -639,6 +674,43 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   slot = next_slot;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
+}
+
+// Merge of split-key partial results: for query row i of a head, the units
+// s = 0 .. last(i) / split_keys (last(i) = i causal, N - 1 otherwise) hold O_s and
+// LSE_s over their keys; LSE = log sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s.
+// One wavefront per row (D/64 features per lane), four rows per workgroup.
+template <int D, bool CAUSAL, bool OF32>
+__global__ void __launch_bounds__(256) attn_merge_kernel(const Params p, int rows_total, int split_keys) {
+  constexpr int F = D / 64;  // features per lane
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows_total) return;
+  const int i = row % p.N;
+  const int last = CAUSAL ? i : p.N - 1;
+  const int ns = min(p.n_splits, last / split_keys + 1);
+  float m = -INFINITY;
+  for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, p.ws_lse[(size_t)sp * p.split_stride + row]);
+  float z = 0.f;
+  float acc[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) acc[f] = 0.f;
+  for (int sp = 0; sp < ns; ++sp) {
+    const float w = __builtin_amdgcn_exp2f((p.ws_lse[(size_t)sp * p.split_stride + row] - m) * 1.44269504088896341f);
+    z += w;
+    const float* o = p.ws_o + ((size_t)sp * p.split_stride + row) * D + F * lane;
+#pragma unroll
+    for (int f = 0; f < F; ++f) acc[f] = fmaf(w, o[f], acc[f]);
+  }
+  const float inv = 1.f / z;
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    if (OF32)
+      ((float*)p.o)[(size_t)row * D + F * lane + f] = acc[f] * inv;
+    else
+      ((__bf16*)p.o)[(size_t)row * D + F * lane + f] = (__bf16)(acc[f] * inv);
+  }
+  if (lane == 0) p.lse[row] = m + logf(z);
 }
 
 }  // namespace attn

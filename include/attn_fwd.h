@@ -46,8 +46,9 @@ extern "C" {
 /* 1: attn_fwd, attn_fwd_ex, attn_fwd_check and helpers.
  * 2: adds attn_fwd_gqa and attn_fwd_gqa_check (grouped-query attention).
  * 3: adds attn_fwd_varlen and attn_fwd_varlen_check (packed variable-length batches).
- * 4: adds attn_bwd and attn_bwd_check (backward pass, declared in attn_bwd.h). */
-#define ATTN_ABI_VERSION 4
+ * 4: adds attn_bwd and attn_bwd_check (backward pass, declared in attn_bwd.h).
+ * 5: adds attn_fwd_splitkv and attn_fwd_splitkv_workspace_size (split keys). */
+#define ATTN_ABI_VERSION 5
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -197,6 +198,41 @@ attn_status_t attn_fwd_varlen_check(const void* q, const void* k, const void* v,
                                     const float* lse, const int* cu_seqlens, int B, int H,
                                     int Hkv, int total, int max_seqlen, int d, int causal,
                                     float scale, const attn_fwd_opts* opts);
+
+/*
+ * attn_fwd_splitkv - attn_fwd_gqa with the keys of every query tile split into
+ * n_splits ranges computed by separate workgroups, for shapes with too few
+ * query tiles to occupy the GPU and for very long sequences (page "FlashAttention
+ * 4: faster, more memory-efficient attention for LLMs", section "Why attention
+ * kernels still dominate LLM cost", on long contexts). Unit s of a query tile
+ * computes O_s and LSE_s over its key range into the workspace (fp32); a second
+ * kernel merges them per row: LSE = log sum_s exp(LSE_s), O = sum_s
+ * exp(LSE_s - LSE) O_s. The result equals attn_fwd_gqa's up to rounding.
+ *   n_splits        : 1 .. 1024, or 0 to pick enough units to give every compute
+ *                     unit one; clamped to the number of 64-key tiles (and
+ *                     reduced so that no unit is empty).
+ *   workspace       : DEVICE buffer, 256-byte aligned, of at least
+ *                     attn_fwd_splitkv_workspace_size(B, H, N, d, n_splits)
+ *                     bytes, owned by the caller; must not overlap any tensor.
+ *                     Its contents on entry are ignored; on return they are
+ *                     unspecified. Calls that share a workspace must not overlap.
+ *                     With one unit per query tile the plain kernel runs and
+ *                     the workspace is not touched (same bits either way).
+ *   opts            : tau and o_dtype as for attn_fwd_ex; exp2_poly_eighths must
+ *                     be 0 and rescale_count NULL (else ATTN_ERR_UNSUPPORTED).
+ * Other arguments and errors as for attn_fwd_gqa; also ATTN_ERR_NULL (no
+ * workspace), ATTN_ERR_MISALIGNED, ATTN_ERR_DIM (workspace too small, n_splits
+ * out of range, B*H*N + 4 above 2^31 - 1), ATTN_ERR_ALIAS (workspace overlaps).
+ * Two kernels are enqueued on `stream`.
+ */
+attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int Hkv, int N, int d, int causal, float scale,
+                               int n_splits, void* workspace, size_t workspace_bytes,
+                               const attn_fwd_opts* opts, void* stream);
+
+/* Workspace bytes attn_fwd_splitkv needs for these sizes (0 for invalid or
+ * empty sizes). Host only. */
+size_t attn_fwd_splitkv_workspace_size(int B, int H, int N, int d, int n_splits);
 
 /* Tile shape the kernel uses for head dim d: query rows per workgroup and keys
  * per KV tile (the granularity of the online softmax and of the rescale

@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(bnd.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.attn_abi_version() == bnd.ABI_VERSION == 4
+    assert lib.attn_abi_version() == bnd.ABI_VERSION == 5
 
 
 def check(*args, **kw):
@@ -250,3 +250,17 @@ def test_bwd_error_codes(patch, code):
     assert bwd_check(*args) == code
     assert bnd.last_error() != ""
     assert bnd.attn_bwd(*args, None) == code
+
+
+def test_splitkv_workspace_size():
+    # 8 key tiles of 64 at N = 512; 2 units of 4 tiles: fp32 O and LSE per unit and row
+    rows = 1 * 2 * 512
+    assert bnd.splitkv_workspace_size(1, 2, 512, 128, 2) == 2 * rows * 128 * 4 + 2 * rows * 4
+    assert bnd.splitkv_workspace_size(1, 2, 512, 128, 3) == bnd.splitkv_workspace_size(1, 2, 512, 128, 3)
+    # 3 requested -> 3 tiles per unit -> 3 units (8 / 3 rounded up)
+    assert bnd.splitkv_workspace_size(1, 2, 512, 64, 3) == 3 * rows * 64 * 4 + 3 * rows * 4
+    # more units than key tiles: clamped to 8
+    assert bnd.splitkv_workspace_size(1, 2, 512, 64, 100) == 8 * rows * 64 * 4 + 8 * rows * 4
+    assert bnd.splitkv_workspace_size(0, 2, 512, 64, 2) == 0
+    assert bnd.splitkv_workspace_size(1, 2, 512, 96, 2) == 0
+    assert bnd.splitkv_workspace_size(1, 2, 512, 64, -1) == 0
