@@ -34,8 +34,8 @@ KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip", "exp2_poly.h")
 # counter reads for a 256 MiB device copy (FETCH x2.0, WRITE x1.0); see
 # profiles/attn_fwd_headline_counters.md. Valid only for the kernel sources
 # with this SHA-256; any change to them reports traffic as null.
-TRAFFIC = {"sources_sha256": "e93797d23a89be5ae574f5e8ae0caba1f1b5ab7c2413b1313b9f62eb0784d670",
-           "fetch_kib": 214600.0, "write_kib": 140800.0, "fetch_scale": 2.0, "write_scale": 1.0}
+TRAFFIC = {"sources_sha256": "a745d2ddf32eff7c6976992f4b63f0662300c9c3acc2647960a12b9e3d3652e4",
+           "fetch_kib": 214350.0, "write_kib": 140800.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def kernel_sources_sha256() -> str:
@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--no-others", action="store_true",
                     help="time only the K headline steps (no other workloads, no sampled timing)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle time")
+    ap.add_argument("--mode", choices=("forward", "backward", "splitkv"), default="forward",
+                    help="backward / splitkv: time only that path on --workload (a dense workload) and print "
+                         "one short JSON line (for profiling); forward: the benchmark line")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (calibrates profiler byte counters)")
     return ap.parse_args()
@@ -280,10 +283,24 @@ def main():
         print("bench.py needs an MI355X (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(1)
     binding.lib()  # fail loudly if the HIP library is missing
-    by_name = dict(inputs.BY_NAME, **{inputs.VARLEN.name: inputs.VARLEN})
+    by_name = dict(inputs.BY_NAME, **{inputs.VARLEN.name: inputs.VARLEN, inputs.LOWOCC.name: inputs.LOWOCC})
     w = by_name[args.workload]
 
     is_varlen = isinstance(w, inputs.VarlenWorkload)
+    if args.mode != "forward":
+        if is_varlen:
+            print("--mode backward/splitkv needs a dense workload", file=sys.stderr)
+            sys.exit(2)
+        if args.mode == "backward":
+            ms = time_backward(w, args.steps, args.warmup)
+            flops = 2.5 * w.flops  # five N^2 d products against the forward's two
+        else:
+            ms = time_split(w, args.steps, args.warmup)
+            flops = w.flops
+        print(json.dumps({"mode": args.mode, "workload": f"{w.name}: {describe(w)} causal={w.causal}",
+                          "steps": args.steps, "ms_per_step": round(ms, 4),
+                          "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}), flush=True)
+        return
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ms = time_workload(w, args.steps, args.warmup)
@@ -304,7 +321,7 @@ def main():
 
     others = {}
     if not args.no_others:
-        for o in by_name.values():
+        for o in inputs.WORKLOADS + [inputs.VARLEN]:
             if o.name == w.name:
                 continue
             oms = time_workload(o, max(5, args.steps // 2), max(3, args.warmup // 2))
@@ -324,11 +341,10 @@ def main():
 
     splitkv = {}
     if not args.no_others:  # split keys on shapes with fewer query tiles than compute units
-        for (B, H, N, d, causal) in ((1, 2, 16384, 128, False), (1, 4, 32768, 128, True)):
-            sw = inputs.Workload(f"lowocc_{N}", B, H, N, d, causal, False, 1100 + H)
+        for sw in (inputs.LOWOCC, inputs.Workload("lowocc_causal32k", 1, 4, 32768, 128, True, False, 1104)):
             plain = time_workload(sw, 10, 3)
             split = time_split(sw, 10, 3)
-            splitkv[sw.name] = {"shape": describe(sw), "causal": causal, "ms_plain": round(plain, 4),
+            splitkv[sw.name] = {"shape": describe(sw), "causal": sw.causal, "ms_plain": round(plain, 4),
                                 "ms_split": round(split, 4),
                                 "tflops_plain": round(sw.flops / (plain * 1e-3) / 1e12, 1),
                                 "tflops_split": round(sw.flops / (split * 1e-3) / 1e12, 1)}

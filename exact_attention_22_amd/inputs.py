@@ -71,6 +71,10 @@ WORKLOADS = [
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
+# Fewer query tiles (2 heads x 64 tiles of 256 rows) than the 256 compute units:
+# the shape split keys are for.
+LOWOCC = Workload("lowocc", 1, 2, 16384, 128, False, False, 1102)
+
 
 def draw(B: int, H: int, N: int, d: int, seed: int, drift: bool = False,
          drift_rate: float = 0.002):
