@@ -62,7 +62,11 @@ struct BwdParams {
   float c;            // scale * log2(e)
 };
 
-constexpr int kWaves = 4;            // one wavefront per SIMD
+// Four wavefronts per workgroup (one per SIMD). The dq kernel (and the dk/dv kernel
+// at D = 64) fits two workgroups per compute unit, so each SIMD runs two wavefronts
+// whose matrix and vector work overlap; the dk/dv kernel at D = 128 holds two
+// 128-feature accumulators per lane and runs one (two would spill).
+constexpr int kWaves = 4;
 constexpr int kRows = 32 * kWaves;   // rows a workgroup owns
 constexpr int kTile = 64;            // rows of the streamed tiles
 
@@ -169,7 +173,7 @@ __device__ __forceinline__ void sync_tiles() {
 // ---------------------------------------------------------------------------
 // dq kernel: workgroup = (b, h, 128 query rows).
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1) attn_bwd_dq_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) {
   constexpr int KK = D / 16, MT = D / 32, NC = kTile / 32;
   constexpr int TB = kTile * D * 2;
   // Separate arrays per buffer (not one [2][TB] array): the compiler then sees that
@@ -222,42 +226,36 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq_kernel(const BwdParams p) 
     const int j0 = t * kTile;
     load_tile64<D>(p.k + kvhead, N, j0 + kTile, Kn, wave, lane);
     load_tile64<D>(p.v + kvhead, N, j0 + kTile, Vn, wave, lane);
-    f32x16 s[NC], dp[NC];
+    const bool edge = j0 + kTile > N || (CAUSAL && j0 + kTile - 1 > i0 + 32 * wave);
+    // One 32-key block at a time, so that only one block's scores are live.
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
-      s[cc] = f32x16{};
-      dp[cc] = f32x16{};
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(K, 32 * cc + l32, 2 * kk + hl), qreg[kk], s[cc],
-                                                        0, 0, 0);
-        dp[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(V, 32 * cc + l32, 2 * kk + hl), doreg[kk],
-                                                         dp[cc], 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(K, 32 * cc + l32, 2 * kk + hl), qreg[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(V, 32 * cc + l32, 2 * kk + hl), doreg[kk], dp, 0, 0,
+                                                     0);
       }
-    }
-    // dS^T in the B-operand order of the next product: k-step 2*cc + hh holds keys
-    // 32*cc + 16*hh + 8*(j/4) + 4*hl + j%4 (register r = 8*hh + j of the block).
-    const bool edge = j0 + kTile > N || (CAUSAL && j0 + kTile - 1 > i0 + 32 * wave);
-    bf16x8 dsb[NC][2];
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
+      // dS^T in the B-operand order of the next product: k-step 2*cc + hh holds keys
+      // 32*cc + 16*hh + 8*(j/4) + 4*hl + j%4 (register r = 8*hh + j of the block).
+      bf16x8 dsb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[cc][r], p.c, -lse2));
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -lse2));
         if (edge) {
           const int key = j0 + 32 * cc + 8 * (r / 4) + 4 * hl + (r % 4);
           pr = (key >= N || (CAUSAL && key > my_q)) ? 0.f : pr;
         }
-        dsb[cc][r / 8][r % 8] = (__bf16)(pr * (dp[cc][r] - Di));
+        dsb[r / 8][r % 8] = (__bf16)(pr * (dp[r] - Di));
       }
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(K, 32 * cc + 16 * hh, 32 * mt, lane),
-                                                            dsb[cc][hh], acc[mt], 0, 0, 0);
+                                                            dsb[hh], acc[mt], 0, 0, 0);
+    }
     sync_tiles();
   };
   int t = 0;
@@ -273,7 +271,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq_kernel(const BwdParams p) 
 // dkdv kernel: workgroup = (b, key/value head g, 128 key rows); walks the query
 // tiles of query heads g*G .. g*G + G - 1.
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(const BwdParams p) {
   constexpr int KK = D / 16, MT = D / 32, NC = kTile / 32;
   constexpr int TB = kTile * D * 2;
   // One array per buffer, as in the dq kernel.
@@ -330,25 +328,19 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdParams p
                   float* ln, float* dn) {
     issue(t + 1, Qn, dOn, ln, dn);
     const int iq0 = (it0 + t % per_head) * kTile;
-    f32x16 s[NC], dp[NC];
+    const bool edge = iq0 + kTile > N || (CAUSAL && iq0 < j0w + 32 * wave + 32);
+    // One 32-query block at a time, so that only one block's scores are live. Lane l
+    // holds key my_k (column) and, in register r, query row 32*cc + 8*(r/4) + 4*hl + r%4.
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
-      s[cc] = f32x16{};
-      dp[cc] = f32x16{};
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Q, 32 * cc + l32, 2 * kk + hl), kreg[kk], s[cc],
-                                                        0, 0, 0);
-        dp[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dO, 32 * cc + l32, 2 * kk + hl), vreg[kk],
-                                                         dp[cc], 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Q, 32 * cc + l32, 2 * kk + hl), kreg[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dO, 32 * cc + l32, 2 * kk + hl), vreg[kk], dp, 0, 0,
+                                                     0);
       }
-    }
-    // Lane l holds key my_k (column) and, in register r of block cc, query row
-    // 32*cc + 8*(r/4) + 4*hl + r%4 of the tile.
-    const bool edge = iq0 + kTile > N || (CAUSAL && iq0 < j0w + 32 * wave + 32);
-    bf16x8 pb[NC][2], dsb[NC][2];
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int qr = 32 * cc + 8 * gq + 4 * hl;
@@ -357,26 +349,25 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdParams p
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * gq + e;
-          float pr = __builtin_amdgcn_exp2f(fmaf(s[cc][r], p.c, -l4[e] * 1.44269504088896341f));
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -l4[e] * 1.44269504088896341f));
           if (edge) {
             const int qi = iq0 + qr + e;
             pr = (qi >= N || (CAUSAL && my_k > qi)) ? 0.f : pr;
           }
-          pb[cc][r / 8][r % 8] = (__bf16)pr;
-          dsb[cc][r / 8][r % 8] = (__bf16)(pr * (dp[cc][r] - d4[e]));
+          pb[r / 8][r % 8] = (__bf16)pr;
+          dsb[r / 8][r % 8] = (__bf16)(pr * (dp[r] - d4[e]));
         }
       }
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           dva[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(dO, 32 * cc + 16 * hh, 32 * mt, lane),
-                                                            pb[cc][hh], dva[mt], 0, 0, 0);
+                                                            pb[hh], dva[mt], 0, 0, 0);
           dka[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(Q, 32 * cc + 16 * hh, 32 * mt, lane),
-                                                            dsb[cc][hh], dka[mt], 0, 0, 0);
+                                                            dsb[hh], dka[mt], 0, 0, 0);
         }
+    }
     sync_tiles();
   };
   int t = 0;
