@@ -18,4 +18,4 @@ from .exact import (  # noqa: F401
     attention_varlen_rows,
     brute_force_attention_varlen,
 )
-from .backward import attention_backward, attention_backward_rows  # noqa: F401
+from .backward import attention_backward, attention_backward_rows, attention_backward_varlen  # noqa: F401

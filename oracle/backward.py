@@ -138,3 +138,37 @@ def _prob_rows(qrows, kh, rows, causal, scale):
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
     return e / e.sum(axis=1, keepdims=True)
+
+
+def attention_backward_varlen(q, k, v, do, cu_seqlens, causal: bool, scale: float):
+    """Backward of packed variable-length attention (layout of oracle/exact.py's
+    attention_varlen: q, do [H,total,d]; k, v [Hkv,total,d]; cu_seqlens [B+1]).
+
+    Every sequence is the per-head backward above on its own rows and keys; key/value
+    gradients of a shared head are summed over its query heads. Returns
+    (dQ [H,total,d], dK [Hkv,total,d], dV [Hkv,total,d], D [H,total]).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    H, T, d = q.shape
+    Hkv = k.shape[0]
+    if do.shape != q.shape or k.shape != (Hkv, T, d) or v.shape != k.shape or Hkv < 1 or H % Hkv:
+        raise ValueError(f"shapes q {q.shape} k {k.shape} v {v.shape} do {do.shape}")
+    cu = np.asarray(cu_seqlens, dtype=np.int64).reshape(-1)
+    if cu.size < 1 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, not decrease and end at total")
+    scale = float(np.float64(scale))
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dd = np.zeros((H, T))
+    for b in range(cu.size - 1):
+        a, e = int(cu[b]), int(cu[b + 1])
+        if e == a:
+            continue
+        for h in range(H):
+            g = kv_head(h, H, Hkv)
+            dq[h, a:e], dkh, dvh, dd[h, a:e] = _head_backward(q[h, a:e], k[g, a:e], v[g, a:e], do[h, a:e], causal,
+                                                               scale)
+            dk[g, a:e] += dkh
+            dv[g, a:e] += dvh
+    return dq, dk, dv, dd

@@ -148,3 +148,55 @@ def test_unmutated_copy_passes(monkeypatch):
     dq, dk, dv, _ = ob.attention_backward(q, k, v, do, True, 0.6)
     fq, fk, fv = fd_gradients(q, k, v, do, True, 0.6)
     assert all(np.max(np.abs(a - b)) <= 1e-7 for a, b in ((dq, fq), (dk, fk), (dv, fv)))
+
+
+def fd_gradients_varlen(q, k, v, do, cu, causal, scale, eps=1e-6):
+    """Central differences of L = sum(O * dO) through the packed forward oracle."""
+    q, k, v, do = (np.array(t, dtype=np.float64) for t in (q, k, v, do))
+
+    def loss():
+        return float((oracle.attention_varlen(q, k, v, cu, causal, scale)[0] * do).sum())
+
+    grads = []
+    for x in (q, k, v):
+        g = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = loss()
+            x[idx] = keep - eps
+            lm = loss()
+            x[idx] = keep
+            g[idx] = (lp - lm) / (2 * eps)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lengths,H,Hkv", [([2, 3], 2, 1), ([1, 0, 3], 2, 2), ([4], 1, 1)])
+def test_varlen_finite_differences(lengths, H, Hkv, causal):
+    T, d = sum(lengths), 2
+    r = np.random.default_rng(sum(lengths) + H + causal)
+    q, do = r.standard_normal((H, T, d)), r.standard_normal((H, T, d))
+    k, v = r.standard_normal((Hkv, T, d)), r.standard_normal((Hkv, T, d))
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    dq, dk, dv, _ = oracle.attention_backward_varlen(q, k, v, do, cu, causal, 0.7)
+    fq, fk, fv = fd_gradients_varlen(q, k, v, do, cu, causal, 0.7)
+    for a, b in ((dq, fq), (dk, fk), (dv, fv)):
+        assert np.max(np.abs(a - b)) <= 1e-7
+
+
+def test_varlen_backward_equal_lengths_is_dense():
+    """B sequences of one length, packed, give the dense backward on [B,H,N,d] (bitwise)."""
+    B, H, Hkv, N, d = 3, 4, 2, 9, 5
+    r = np.random.default_rng(61)
+    q, do = r.standard_normal((B, H, N, d)), r.standard_normal((B, H, N, d))
+    k, v = r.standard_normal((B, Hkv, N, d)), r.standard_normal((B, Hkv, N, d))
+    pack = lambda t: t.transpose(1, 0, 2, 3).reshape(t.shape[1], B * N, d)
+    cu = np.arange(B + 1) * N
+    for causal in (False, True):
+        got = oracle.attention_backward_varlen(pack(q), pack(k), pack(v), pack(do), cu, causal, 0.4)
+        ref = oracle.attention_backward(q, k, v, do, causal, 0.4)
+        for x, y in zip(got[:3], ref[:3]):
+            assert np.array_equal(x, pack(y))
+        assert np.array_equal(got[3], ref[3].transpose(1, 0, 2).reshape(H, B * N))
