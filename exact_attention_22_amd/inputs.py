@@ -23,6 +23,13 @@ cu_seqlens. `varlen_lengths` draws B lengths log-uniformly between lo and hi
 (integers, so most are not multiples of any tile size).
   varlen    24 sequences of 64 .. 8192 tokens (seed 1007), 32 query heads,
             8 key/value heads, d = 128, causal.
+
+FP8 inputs (`draw_fp8`): the same N(0,1) draws in float32, each tensor
+quantised once to OCP e4m3 ("e4m3fn") codes with one per-tensor scale,
+amax / 448 (448 is e4m3's largest finite value), by torch's round-to-nearest
+conversion. V is handed over transposed, [B, H, d, ldv] with ldv = N rounded up
+to a multiple of 16; columns N .. ldv-1 are padding that neither side reads.
+  fp8_headline  2 x 32 x 8192 x 128 non-causal (seed 1003, the headline draw)
 """
 from __future__ import annotations
 
@@ -163,6 +170,48 @@ VARLEN = VarlenWorkload("varlen", 24, 64, 8192, 32, 8, 128, True, 1007)
 def workload_inputs(w: Workload, seed: int | None = None):
     """Inputs of a named workload (its own seed unless one is given)."""
     return draw_gqa(w.B, w.H, w.kv_heads, w.N, w.d, w.seed if seed is None else seed, w.drift)
+
+
+E4M3_MAX = 448.0
+
+
+def fp8_ldv(N: int) -> int:
+    """Row length of the transposed V operand: N rounded up to a multiple of 16."""
+    return (N + 15) // 16 * 16
+
+
+def quantize_e4m3(x: torch.Tensor):
+    """(codes, scale): x (float32) ~= decode(codes) * scale, with one float32 scale
+    amax / 448 per tensor. Codes are uint8 e4m3fn bit patterns."""
+    amax = float(x.abs().max()) if x.numel() else 0.0
+    scale = float(torch.tensor(amax / E4M3_MAX if amax > 0 else 1.0, dtype=torch.float32))
+    y = (x / scale).clamp(-E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8), scale
+
+
+def draw_fp8(B: int, H: int, N: int, d: int, seed: int, drift: bool = False, pad_code: int = 0):
+    """FP8 attention inputs from the same float32 draws as `draw` (same seed, same order):
+    q8, k8 uint8 [B,H,N,d], vt8 uint8 [B,H,d,ldv] (V transposed, padding columns set to
+    pad_code) and the three per-tensor scales (q_scale, k_scale, v_scale)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    if drift:
+        u = torch.full((d,), 1.0 / math.sqrt(d), dtype=torch.float32)
+        j = torch.arange(N, dtype=torch.float32).view(1, 1, N, 1)
+        k += 0.002 * j * u
+        q += u
+    q8, qs = quantize_e4m3(q)
+    k8, ks = quantize_e4m3(k)
+    v8, vs = quantize_e4m3(v)
+    ldv = fp8_ldv(N)
+    vt8 = torch.full((B, H, d, ldv), pad_code, dtype=torch.uint8)
+    vt8[..., :N] = v8.transpose(-1, -2)
+    return q8, k8, vt8, (qs, ks, vs)
+
+
+FP8_HEADLINE = Workload("fp8_headline", 2, 32, 8192, 128, False, False, 1003)
 
 
 def digest(*tensors) -> str:

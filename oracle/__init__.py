@@ -18,4 +18,5 @@ from .exact import (  # noqa: F401
     attention_varlen_rows,
     brute_force_attention_varlen,
 )
+from .fp8 import attention_fp8, attention_fp8_rows, fp8_error_bound, fp8_error_bound_rows, e4m3_decode  # noqa: F401
 from .backward import attention_backward, attention_backward_rows, attention_backward_varlen  # noqa: F401
