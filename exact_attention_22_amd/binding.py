@@ -24,8 +24,9 @@ O_BF16, O_F32 = 0, 1
 EXPORTS = ["attn_fwd", "attn_fwd_ex", "attn_fwd_check", "attn_fwd_opts_init", "attn_status_str",
            "attn_last_error", "attn_abi_version", "attn_exp2_poly_host", "attn_fwd_tile_shape",
            "attn_fwd_gqa", "attn_fwd_gqa_check", "attn_fwd_varlen", "attn_fwd_varlen_check",
-           "attn_bwd", "attn_bwd_check", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size"]
-ABI_VERSION = 5
+           "attn_bwd", "attn_bwd_check", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size",
+           "attn_fwd_fp8", "attn_fwd_fp8_check"]
+ABI_VERSION = 6
 
 
 class AttnFwdOpts(ctypes.Structure):
@@ -78,6 +79,11 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.restype = i
         L.attn_bwd_check.argtypes = bwd_args
         L.attn_bwd_check.restype = i
+        fp8_args = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, f, f, f]
+        L.attn_fwd_fp8.argtypes = fp8_args + [vp]
+        L.attn_fwd_fp8.restype = i
+        L.attn_fwd_fp8_check.argtypes = fp8_args
+        L.attn_fwd_fp8_check.restype = i
         L.attn_fwd_opts_init.argtypes = [ctypes.POINTER(AttnFwdOpts)]
         L.attn_fwd_opts_init.restype = None
         L.attn_status_str.argtypes = [i]
@@ -341,6 +347,64 @@ def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
     st = lib().attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
                                 Hkv, N, d, int(causal), scale, n_splits, workspace.data_ptr(),
                                 workspace.numel() * workspace.element_size(), ctypes.byref(opts), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, last_error())
+    return out, lse
+
+
+def attn_fwd_fp8(q, k, vt, o, lse, B, H, N, d, causal, scale, q_scale, k_scale, v_scale, tau, stream) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return lib().attn_fwd_fp8(q, k, vt, o, lse, B, H, N, d, int(causal), scale, q_scale, k_scale, v_scale, tau,
+                              stream)
+
+
+def attn_fwd_fp8_check(q, k, vt, o, lse, B, H, N, d, causal, scale, q_scale, k_scale, v_scale, tau) -> int:
+    return lib().attn_fwd_fp8_check(q, k, vt, o, lse, B, H, N, d, int(causal), scale, q_scale, k_scale, v_scale,
+                                    tau)
+
+
+def fp8_ldv(N: int) -> int:
+    """Row length of the transposed V operand: N rounded up to a multiple of 16."""
+    return (N + 15) // 16 * 16
+
+
+def attention_fp8(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, scales, causal: bool = False,
+                  scale: float | None = None, *, tau: float = 8.0, out: torch.Tensor | None = None,
+                  lse: torch.Tensor | None = None):
+    """FP8 exact attention forward on the current stream: returns (O bf16 [B,H,N,d], LSE fp32 [B,H,N]).
+
+    q, k: e4m3 codes [B,H,N,d] (uint8 or torch.float8_e4m3fn); vt: V transposed, e4m3 codes
+    [B,H,d,ldv] with ldv = fp8_ldv(N) (padding columns unused); scales = (q_scale, k_scale,
+    v_scale), the per-tensor dequantisation factors; scale defaults to 1/sqrt(d).
+    """
+    def codes(name, t):
+        if not isinstance(t, torch.Tensor) or t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{name} must be a uint8 or float8_e4m3fn tensor")
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise TypeError(f"{name} must be a contiguous 4-d CUDA tensor")
+        return t
+    codes("q", q)
+    B, H, N, d = q.shape
+    codes("k", k)
+    codes("vt", vt)
+    if tuple(k.shape) != (B, H, N, d):
+        raise ValueError(f"k must be [{B},{H},{N},{d}], got {tuple(k.shape)}")
+    if tuple(vt.shape) != (B, H, d, fp8_ldv(N)):
+        raise ValueError(f"vt must be [{B},{H},{d},{fp8_ldv(N)}], got {tuple(vt.shape)}")
+    if k.device != q.device or vt.device != q.device:
+        raise ValueError("q, k and vt must be on one device")
+    qs, ks, vs = (float(x) for x in scales)
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+    out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, N, d) or not out.is_contiguous():
+        raise TypeError("out must be a contiguous bfloat16 [B,H,N,d] tensor")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 [B,H,N] tensor")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_fwd_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                      causal, scale, qs, ks, vs, tau, stream)
     if st != ATTN_OK:
         raise AttnError(st, last_error())
     return out, lse

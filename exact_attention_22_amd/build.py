@@ -34,7 +34,8 @@ def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False)
     tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", *HIP_FLAGS, "-shared",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_bwd.hip"), "-o", tmp, *(extra or [])]
+           os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_bwd.hip"),
+           os.path.join(CSRC, "attn_fp8.hip"), "-o", tmp, *(extra or [])]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,100 @@
+// attn_fp8.hip - C ABI, argument checks and launch of the gfx950 FP8 attention
+// forward kernel (attn_fp8_kernel.h). The contract is documented in
+// include/attn_fp8.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_fp8.h"
+#include "attn_fp8_kernel.h"
+#include "attn_host.h"
+
+namespace {
+
+using attn_host::fail;
+using attn_host::overlaps;
+
+attn_status_t validate(const void* q, const void* k, const void* vt, const void* o, const float* lse, int B, int H,
+                       int N, int d, float scale, float qs, float ks, float vs, float tau, bool* work) {
+  attn_host::clear_error();
+  *work = false;
+  if (B < 0 || H < 0 || N < 0) return fail(ATTN_ERR_DIM, "negative size B=%d H=%d N=%d", B, H, N);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  if (!(tau >= 0.f && tau <= 8.f)) return fail(ATTN_ERR_UNSUPPORTED, "tau=%g outside [0, 8]", (double)tau);
+  const float sc[4] = {scale, qs, ks, vs};
+  for (float x : sc)
+    if (!isfinite(x) || !(x > 0.f)) return fail(ATTN_ERR_SCALE, "scales must be finite and positive");
+  const float c = scale * qs * ks * 1.44269504088896341f;
+  if (!isnormal(c)) return fail(ATTN_ERR_SCALE, "scale * q_scale * k_scale is not a normal fp32 value");
+  if ((int64_t)B * H * N == 0) return ATTN_OK;
+  const int64_t rows = (int64_t)B * H * N;
+  const int64_t ldv = ((int64_t)N + 15) / 16 * 16;
+  const int64_t tiles = (int64_t)B * H * ((N + attn_fp8::kRows - 1) / attn_fp8::kRows);
+  if (rows > (int64_t)1 << 40 || tiles > INT32_MAX / 2 || ldv > INT32_MAX)
+    return fail(ATTN_ERR_DIM, "problem too large: B*H*N=%lld", (long long)rows);
+  if (!q || !k || !vt || !o || !lse) return fail(ATTN_ERR_NULL, "NULL tensor pointer");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)vt | (uintptr_t)o) & 15)
+    return fail(ATTN_ERR_MISALIGNED, "q, k, vt and o must be 16-byte aligned");
+  if ((uintptr_t)lse & 3) return fail(ATTN_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  const size_t qb = (size_t)rows * d, vb = (size_t)B * H * d * ldv, ob = (size_t)rows * d * 2, lb = (size_t)rows * 4;
+  const void* ins[3] = {q, k, vt};
+  const size_t in_b[3] = {qb, qb, vb};
+  for (int j = 0; j < 3; ++j)
+    if (overlaps(o, ob, ins[j], in_b[j]) || overlaps(lse, lb, ins[j], in_b[j]))
+      return fail(ATTN_ERR_ALIAS, "an output overlaps an input");
+  if (overlaps(o, ob, lse, lb)) return fail(ATTN_ERR_ALIAS, "o overlaps lse");
+  *work = true;
+  return ATTN_OK;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const attn_fp8::Fp8Params& p, hipStream_t stream) {
+  void* args[] = {const_cast<attn_fp8::Fp8Params*>(&p)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fp8::attn_fwd_fp8_kernel<D, CAUSAL>),
+                         dim3(8 * p.per_xcd), dim3(64 * attn_fp8::kWaves), args, 0, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd_fp8_check(const void* q, const void* k, const void* vt, const void* o, const float* lse, int B,
+                                 int H, int N, int d, int causal, float scale, float q_scale, float k_scale,
+                                 float v_scale, float tau) {
+  (void)causal;
+  bool work;
+  return validate(q, k, vt, o, lse, B, H, N, d, scale, q_scale, k_scale, v_scale, tau, &work);
+}
+
+attn_status_t attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, int B, int H, int N,
+                           int d, int causal, float scale, float q_scale, float k_scale, float v_scale, float tau,
+                           void* stream) {
+  bool work = false;
+  const attn_status_t st = validate(q, k, vt, o, lse, B, H, N, d, scale, q_scale, k_scale, v_scale, tau, &work);
+  if (st != ATTN_OK || !work) return st;
+  attn_fp8::Fp8Params p;
+  p.q = (const uint8_t*)q;
+  p.k = (const uint8_t*)k;
+  p.vt = (const uint8_t*)vt;
+  p.o = (__bf16*)o;
+  p.lse = lse;
+  p.N = N;
+  p.ldv = (N + 15) / 16 * 16;
+  p.nq_tiles = (N + attn_fp8::kRows - 1) / attn_fp8::kRows;
+  p.total_tiles = B * H * p.nq_tiles;
+  p.per_xcd = (p.total_tiles + 7) / 8;
+  p.c = scale * q_scale * k_scale * 1.44269504088896341f;
+  p.ov = v_scale;
+  p.tau = tau;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (d == 128)
+    e = causal ? launch<128, true>(p, s) : launch<128, false>(p, s);
+  else
+    e = causal ? launch<64, true>(p, s) : launch<64, false>(p, s);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+}  // extern "C"

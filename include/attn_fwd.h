@@ -47,8 +47,9 @@ extern "C" {
  * 2: adds attn_fwd_gqa and attn_fwd_gqa_check (grouped-query attention).
  * 3: adds attn_fwd_varlen and attn_fwd_varlen_check (packed variable-length batches).
  * 4: adds attn_bwd and attn_bwd_check (backward pass, declared in attn_bwd.h).
- * 5: adds attn_fwd_splitkv and attn_fwd_splitkv_workspace_size (split keys). */
-#define ATTN_ABI_VERSION 5
+ * 5: adds attn_fwd_splitkv and attn_fwd_splitkv_workspace_size (split keys).
+ * 6: adds attn_fwd_fp8 and attn_fwd_fp8_check (FP8 e4m3 inputs, declared in attn_fp8.h). */
+#define ATTN_ABI_VERSION 6
 
 typedef enum attn_status {
   ATTN_OK = 0,

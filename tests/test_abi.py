@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(bnd.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.attn_abi_version() == bnd.ABI_VERSION == 5
+    assert lib.attn_abi_version() == bnd.ABI_VERSION == 6
 
 
 def check(*args, **kw):
@@ -264,3 +264,39 @@ def test_splitkv_workspace_size():
     assert bnd.splitkv_workspace_size(0, 2, 512, 64, 2) == 0
     assert bnd.splitkv_workspace_size(1, 2, 512, 96, 2) == 0
     assert bnd.splitkv_workspace_size(1, 2, 512, 64, -1) == 0
+
+
+def fp8_check(**kw):
+    a = dict(q=Q, k=K, vt=V, o=O, lse=L, B=2, H=32, N=8192, d=128, causal=0, scale=0.088, q_scale=0.01,
+             k_scale=0.01, v_scale=0.01, tau=8.0)
+    a.update(kw)
+    return bnd.attn_fwd_fp8_check(*a.values())
+
+
+def test_fp8_valid_and_empty():
+    assert fp8_check() == bnd.ATTN_OK
+    assert fp8_check(N=77, d=64, causal=1, tau=0.0) == bnd.ATTN_OK
+    assert fp8_check(q=None, k=None, vt=None, o=None, lse=None, N=0) == bnd.ATTN_OK
+    assert bnd.attn_fwd_fp8(None, None, None, None, None, 0, 1, 16, 64, 0, 1.0, 1.0, 1.0, 1.0, 8.0, None) == bnd.ATTN_OK
+
+
+@pytest.mark.parametrize("patch,code", [
+    (dict(q=None), 1), (dict(lse=None), 1),
+    (dict(B=-1), 2), (dict(N=-3), 2), (dict(B=1 << 20, H=1 << 10, N=1 << 20), 2),
+    (dict(d=96), 3), (dict(tau=8.5), 3), (dict(tau=-1.0), 3), (dict(tau=float("nan")), 3),
+    (dict(q=Q + 8), 4), (dict(vt=V + 4), 4), (dict(lse=L + 2), 4),
+    (dict(scale=0.0), 5), (dict(scale=-1.0), 5), (dict(q_scale=float("inf")), 5), (dict(v_scale=0.0), 5),
+    (dict(scale=1e-30, q_scale=1e-10, k_scale=1e-10), 5),
+    (dict(o=Q + 64), 6), (dict(lse=V + 1024), 6), (dict(lse=O + 4096), 6),
+])
+def test_fp8_error_codes(patch, code):
+    assert fp8_check(**patch) == code
+
+
+def test_fp8_alias_uses_transposed_padded_extent():
+    # vt spans B*H*d*ldv bytes with ldv = 8208 for N = 8193: an lse placed inside its padding overlaps
+    B, H, N, d = 1, 1, 8193, 64
+    ldv = bnd.fp8_ldv(N)
+    assert ldv == 8208
+    assert fp8_check(B=B, H=H, N=N, d=d, lse=V + d * ldv - 16) == 6
+    assert fp8_check(B=B, H=H, N=N, d=d, lse=V + d * ldv) == bnd.ATTN_OK
