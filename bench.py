@@ -25,6 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "exact_attention_22_amd", "csrc")
 KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip", "exp2_poly.h")
@@ -71,7 +72,7 @@ def parse():
     ap.add_argument("--no-others", action="store_true",
                     help="time only the K headline steps (no other workloads, no sampled timing)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle time")
-    ap.add_argument("--mode", choices=("forward", "backward", "splitkv"), default="forward",
+    ap.add_argument("--mode", choices=("forward", "backward", "splitkv", "fp8"), default="forward",
                     help="backward / splitkv: time only that path on --workload (a dense workload) and print "
                          "one short JSON line (for profiling); forward: the benchmark line")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -192,6 +193,37 @@ def time_split(w, steps, warmup):
     return ms
 
 
+def time_fp8(w, steps, warmup):
+    """Average time (ms) of attn_fwd_fp8 on a dense workload's shape: the same N(0,1)
+    draws quantised to e4m3 with per-tensor scales, V transposed."""
+    import torch
+
+    from exact_attention_22_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    q8, k8, vt8, sc = inputs.draw_fp8(w.B, w.H, w.N, w.d, seed=w.seed, drift=w.drift)
+    q8, k8, vt8 = q8.to(dev), k8.to(dev), vt8.to(dev)
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def call():
+        binding.attention_fp8(q8, k8, vt8, sc, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del q8, k8, vt8, o, lse
+    torch.cuda.empty_cache()
+    return ms
+
+
 def time_samples(w, n_samples=20, min_ms=50.0):
     """n_samples timed batches of back-to-back launches, each at least min_ms long;
     per-launch median and min (ms)."""
@@ -294,6 +326,13 @@ def main():
         if args.mode == "backward":
             ms = time_backward(w, args.steps, args.warmup)
             flops = 2.5 * w.flops  # five N^2 d products against the forward's two
+        elif args.mode == "fp8":
+            ms = time_fp8(w, args.steps, args.warmup)
+            flops = w.flops
+            if args.copy_mib:  # calibration copy for the profiler's byte counters
+                src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda:0")
+                torch.empty_like(src).copy_(src)
+                torch.cuda.synchronize()
         else:
             ms = time_split(w, args.steps, args.warmup)
             flops = w.flops
@@ -349,6 +388,15 @@ def main():
                                 "tflops_plain": round(sw.flops / (plain * 1e-3) / 1e12, 1),
                                 "tflops_split": round(sw.flops / (split * 1e-3) / 1e12, 1)}
 
+    fp8 = {}
+    if not args.no_others:  # FP8 (e4m3) forward, against the dense fp8 matrix-core peak
+        for name in ("headline", "causal2k", "long32k", "drift8k"):
+            o = inputs.BY_NAME[name]
+            fms = time_fp8(o, max(5, args.steps // 2), 3)
+            ft = o.flops / (fms * 1e-3) / 1e12
+            fp8[name] = {"ms": round(fms, 4), "tflops": round(ft, 1), "frac_peak_fp8": round(ft / PEAK_FP8_TFLOPS, 4),
+                         "causal": o.causal, "shape": describe(o)}
+
     line = {
         "metric": "attention fwd TFLOP/s (bf16, causal & non-causal) and % of MI355X MFMA peak",
         "value": round(tflops, 2),
@@ -374,6 +422,7 @@ def main():
         "workloads": others,
         "backward": backward,
         "splitkv": splitkv,
+        "fp8": fp8,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -30,7 +30,7 @@ attn_status_t validate(const void* q, const void* k, const void* vt, const void*
   if ((int64_t)B * H * N == 0) return ATTN_OK;
   const int64_t rows = (int64_t)B * H * N;
   const int64_t ldv = ((int64_t)N + 15) / 16 * 16;
-  const int64_t tiles = (int64_t)B * H * ((N + attn_fp8::kRows - 1) / attn_fp8::kRows);
+  const int64_t tiles = (int64_t)B * H * ((N + attn_fp8::kMinRows - 1) / attn_fp8::kMinRows);
   if (rows > (int64_t)1 << 40 || tiles > INT32_MAX / 2 || ldv > INT32_MAX)
     return fail(ATTN_ERR_DIM, "problem too large: B*H*N=%lld", (long long)rows);
   if (!q || !k || !vt || !o || !lse) return fail(ATTN_ERR_NULL, "NULL tensor pointer");
@@ -52,7 +52,7 @@ template <int D, bool CAUSAL>
 hipError_t launch(const attn_fp8::Fp8Params& p, hipStream_t stream) {
   void* args[] = {const_cast<attn_fp8::Fp8Params*>(&p)};
   return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fp8::attn_fwd_fp8_kernel<D, CAUSAL>),
-                         dim3(8 * p.per_xcd), dim3(64 * attn_fp8::kWaves), args, 0, stream);
+                         dim3(8 * p.per_xcd), dim3(64 * attn_fp8::Shape<D>::NW), args, 0, stream);
 }
 
 }  // namespace
@@ -81,7 +81,8 @@ attn_status_t attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o
   p.lse = lse;
   p.N = N;
   p.ldv = (N + 15) / 16 * 16;
-  p.nq_tiles = (N + attn_fp8::kRows - 1) / attn_fp8::kRows;
+  const int rows = d == 128 ? attn_fp8::Shape<128>::ROWS : attn_fp8::Shape<64>::ROWS;
+  p.nq_tiles = (N + rows - 1) / rows;
   p.total_tiles = B * H * p.nq_tiles;
   p.per_xcd = (p.total_tiles + 7) / 8;
   p.c = scale * q_scale * k_scale * 1.44269504088896341f;

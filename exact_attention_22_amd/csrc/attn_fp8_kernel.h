@@ -60,9 +60,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kRows = 32 * kWaves;  // query rows per workgroup
-constexpr int kBC = 64;             // keys per tile
+// Wavefronts per workgroup (32 query rows each) for head dim D. Eight wavefronts
+// at D = 128 (one workgroup per compute unit instead of two) measured within 2 %.
+template <int D>
+struct Shape {
+  static constexpr int NW = 4;
+  static constexpr int ROWS = 32 * NW;  // query rows per workgroup
+};
+constexpr int kMinRows = 128;  // smallest Shape<D>::ROWS
+constexpr int kBC = 64;        // keys per tile
 
 struct Fp8Params {
   const uint8_t* q;   // [B][H][N][D] e4m3
@@ -72,7 +78,7 @@ struct Fp8Params {
   float* lse;         // [B][H][N]
   int N;
   int ldv;
-  int nq_tiles;       // ceil(N / kRows)
+  int nq_tiles;       // ceil(N / Shape<D>::ROWS)
   int total_tiles;    // B * H * nq_tiles
   int per_xcd;        // ceil(total_tiles / 8)
   float c;            // scale * q_scale * k_scale * log2(e) (> 0)
@@ -85,14 +91,20 @@ __device__ __forceinline__ f32x16 mma(const i32x8& a, const i32x8& b, const f32x
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// 16-byte chunk swizzles of the LDS tiles; each gives 16 consecutive rows read
-// at one logical chunk 16 distinct 16-byte bank groups (256 bytes of banks).
-// K tile rows are D bytes; V^T tile rows are 64 bytes (4 chunks).
+// 16-byte chunk swizzles of the LDS tiles (chunk c of row r is stored at chunk
+// position c ^ swz(r)). The reads take one logical chunk of 16 consecutive
+// rows per 16 lanes (or of 8 rows per 8 lanes); the V^T writes put 8-byte runs
+// of 4 or 8 consecutive rows at two chunk positions. The swizzles below make
+// all of these hit distinct banks whether the LDS serves 128 or 256 bytes per
+// pass (checked on the CPU against both bank models).
+// 128-byte rows (K at D = 128): chunk bits 0..2 from the row, bit 0 also from row bit 3.
+// 64-byte rows (V^T, and K at D = 64): with a, b, c = row bits 1, 2, 3:
+//   swz = 2 * (a ^ b) + (b ^ c).
+__device__ __forceinline__ int vswz(int r) { return ((((r >> 1) ^ (r >> 2)) & 1) << 1) | (((r >> 2) ^ (r >> 3)) & 1); }
 template <int D>
 __device__ __forceinline__ int kswz(int r) {
-  return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+  return D == 128 ? ((r & 7) ^ ((r >> 3) & 1)) : vswz(r);
 }
-__device__ __forceinline__ int vswz(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -106,43 +118,47 @@ __device__ __forceinline__ float pair_sum(float x) {
 // Per-thread staging of one tile: K rows (D bytes each) and V^T rows (64 keys each).
 template <int D>
 struct Stage {
-  static constexpr int KCH = kBC * D / 16 / (64 * kWaves);  // 16-byte K chunks per thread
-  static constexpr int VCH = D * kBC / 16 / (64 * kWaves);  // 16-byte V^T chunks per thread
+  static constexpr int NT = 64 * Shape<D>::NW;  // threads
+  static constexpr int KCH = kBC * D / 16 / NT;  // 16-byte K chunks per thread
+  static constexpr int VCH = D * kBC / 16 / NT;  // 16-byte V^T chunks per thread
+  static_assert(KCH * NT * 16 == kBC * D && VCH * NT * 16 == D * kBC, "tile split");
   u32x4 kc[KCH];
   u32x4 vc[VCH];
 };
 
+// Buffer resource over `bytes` bytes at `base` (raw loads past the end return zeros;
+// DATA_FORMAT = 32-bit in the third descriptor word, as raw loads require).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Loads of the tile at key j0. K: a resource starting at row j0 and ending at row N,
+// so rows past N read as zeros. V^T: a resource over the rest of the head from
+// column j0; the per-thread offsets (koff, voff) are fixed for the whole kernel.
+// Chunks at or past column N (only in the last tile) may hold padding or the next
+// row's keys; `edge` zeroes those bytes (N - key bytes of the chunk are real keys).
 template <int D>
 __device__ __forceinline__ void stage_load(Stage<D>& st, const uint8_t* kh, const uint8_t* vth, int N, int ldv, int j0,
-                                           int tid) {
-  constexpr int KCPR = D / 16;  // K chunks per row
+                                           const uint32_t (&koff)[Stage<D>::KCH],
+                                           const uint32_t (&voff)[Stage<D>::VCH], int vkey, bool edge) {
+  const __amdgpu_buffer_rsrc_t kr = rsrc(kh + (size_t)j0 * D, (uint32_t)(N - j0) * D);
+  const __amdgpu_buffer_rsrc_t vr = rsrc(vth + j0, (uint32_t)(D * ldv - j0));
 #pragma unroll
-  for (int i = 0; i < Stage<D>::KCH; ++i) {
-    const int id = tid + i * 64 * kWaves;
-    const int row = id / KCPR, ch = id % KCPR;
-    const int key = j0 + row;
-    st.kc[i] = key < N ? *(const u32x4*)(kh + (size_t)key * D + 16 * ch) : u32x4{0, 0, 0, 0};
-  }
+  for (int i = 0; i < Stage<D>::KCH; ++i)
+    st.kc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], 0, 0));
 #pragma unroll
-  for (int i = 0; i < Stage<D>::VCH; ++i) {
-    const int id = tid + i * 64 * kWaves;
-    const int f = id >> 2, jc = id & 3;
-    const int key = j0 + 16 * jc;
-    u32x4 w = u32x4{0, 0, 0, 0};
-    if (key < N) {
-      // key < N <= ldv and both multiples of 16 (key) or rounded up (ldv): the 16 bytes are in bounds
-      w = *(const u32x4*)(vth + (size_t)f * ldv + key);
-      const int valid = N - key;  // bytes of this chunk that are real keys
-      if (valid < 16) {
+  for (int i = 0; i < Stage<D>::VCH; ++i)
+    st.vc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0));
+  if (edge) {
+    const int valid = N - (j0 + vkey);  // real keys in this thread's V^T chunks (same column for every i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int keep = valid - 4 * e;  // bytes kept in word e
-          const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u);
-          w[e] &= m;
-        }
+    for (int i = 0; i < Stage<D>::VCH; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int keep = valid - 4 * e;  // bytes kept in word e
+        const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u);
+        st.vc[i][e] &= m;
       }
-    }
-    st.vc[i] = w;
   }
 }
 
@@ -151,13 +167,13 @@ __device__ __forceinline__ void stage_store(const Stage<D>& st, char* kb, char* 
   constexpr int KCPR = D / 16;
 #pragma unroll
   for (int i = 0; i < Stage<D>::KCH; ++i) {
-    const int id = tid + i * 64 * kWaves;
+    const int id = tid + i * Stage<D>::NT;
     const int row = id / KCPR, ch = id % KCPR;
     *(u32x4*)(kb + row * D + ((ch ^ kswz<D>(row)) << 4)) = st.kc[i];
   }
 #pragma unroll
   for (int i = 0; i < Stage<D>::VCH; ++i) {
-    const int id = tid + i * 64 * kWaves;
+    const int id = tid + i * Stage<D>::NT;
     const int f = id >> 2, jc = id & 3;
     // keys 16jc + e: e in {0..3, 8..11} (h = 0) and {4..7, 12..15} (h = 1); each set
     // lands as 8 contiguous bytes at column 32h + 16*(jc/2) + 8*(jc%2)
@@ -178,7 +194,8 @@ __device__ __forceinline__ i32x8 read32(const char* base, int r, int ch, int swz
 }
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2) attn_fwd_fp8_kernel(const Fp8Params p) {
+__global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_fp8_kernel(const Fp8Params p) {
+  constexpr int kRows = Shape<D>::ROWS;
   constexpr int MQ = D / 64;  // QK products per 32-key block
   constexpr int MT = D / 32;  // PV products (value-feature blocks)
   __shared__ __attribute__((aligned(16))) char kbuf[2][kBC * D];
@@ -228,14 +245,27 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_fp8_kernel(const Fp8Params p)
   const float c = p.c, tau = p.tau;
 
   Stage<D> stg;
-  stage_load<D>(stg, kh, vth, N, p.ldv, 0, tid);
+  uint32_t koff[Stage<D>::KCH], voff[Stage<D>::VCH];
+#pragma unroll
+  for (int i = 0; i < Stage<D>::KCH; ++i) {
+    const int id = tid + i * Stage<D>::NT;
+    koff[i] = (uint32_t)((id / (D / 16)) * D + 16 * (id % (D / 16)));
+  }
+  // V^T chunk id: feature id / 4, keys 16 * (id % 4) .. +15; id % 4 is the same for every i
+  const int vkey = 16 * (tid & 3);
+#pragma unroll
+  for (int i = 0; i < Stage<D>::VCH; ++i) {
+    const int id = tid + i * Stage<D>::NT;
+    voff[i] = (uint32_t)((id >> 2) * p.ldv + 16 * (id & 3));
+  }
+  stage_load<D>(stg, kh, vth, N, p.ldv, 0, koff, voff, vkey, kBC > N);
   stage_store<D>(stg, kbuf[0], vbuf[0], tid);
   __syncthreads();
 
   for (int t = 0; t < nt; ++t) {
     const int j0 = t * kBC;
     const bool more = t + 1 < nt;
-    if (more) stage_load<D>(stg, kh, vth, N, p.ldv, j0 + kBC, tid);
+    if (more) stage_load<D>(stg, kh, vth, N, p.ldv, j0 + kBC, koff, voff, vkey, j0 + 2 * kBC > N);
     const char* kb = kbuf[t & 1];
     const char* vb = vbuf[t & 1];
 
