@@ -52,6 +52,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn_fp8 {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -262,12 +264,15 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
   stage_store<D>(stg, kbuf[0], vbuf[0], tid);
   __syncthreads();
 
-  for (int t = 0; t < nt; ++t) {
+  // One tile step; the loop below is unrolled by two so that each step's LDS buffer
+  // (BUF) is a compile-time constant and the LDS addresses fold into the instructions.
+  auto step = [&](auto buf_tag, int t) {
+    constexpr int BUF = decltype(buf_tag)::value;
     const int j0 = t * kBC;
     const bool more = t + 1 < nt;
     if (more) stage_load<D>(stg, kh, vth, N, p.ldv, j0 + kBC, koff, voff, vkey, j0 + 2 * kBC > N);
-    const char* kb = kbuf[t & 1];
-    const char* vb = vbuf[t & 1];
+    const char* kb = kbuf[BUF];
+    const char* vb = vbuf[BUF];
 
     // S^T = K Q^T for the two 32-key blocks
     f32x16 s[2];
@@ -334,9 +339,14 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
       oacc[mt] = mma(read32<kBC>(vb, f, 2 * hl, vswz(f)), pb, oacc[mt]);
     }
 
-    if (more) stage_store<D>(stg, kbuf[(t + 1) & 1], vbuf[(t + 1) & 1], tid);
+    if (more) stage_store<D>(stg, kbuf[BUF ^ 1], vbuf[BUF ^ 1], tid);
     __syncthreads();
+  };
+  for (int t = 0; t < nt; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < nt) step(std::integral_constant<int, 1>{}, t + 1);
   }
+
 
   const float l_tot = pair_sum(l_sum);
   if (my_q < N) {
