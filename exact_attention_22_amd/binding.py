@@ -25,8 +25,8 @@ EXPORTS = ["attn_fwd", "attn_fwd_ex", "attn_fwd_check", "attn_fwd_opts_init", "a
            "attn_last_error", "attn_abi_version", "attn_exp2_poly_host", "attn_fwd_tile_shape",
            "attn_fwd_gqa", "attn_fwd_gqa_check", "attn_fwd_varlen", "attn_fwd_varlen_check",
            "attn_bwd", "attn_bwd_check", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size",
-           "attn_fwd_fp8", "attn_fwd_fp8_check"]
-ABI_VERSION = 6
+           "attn_fwd_fp8", "attn_fwd_fp8_check", "attn_bwd_varlen", "attn_bwd_varlen_check"]
+ABI_VERSION = 7
 
 
 class AttnFwdOpts(ctypes.Structure):
@@ -79,6 +79,11 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.restype = i
         L.attn_bwd_check.argtypes = bwd_args
         L.attn_bwd_check.restype = i
+        bwdv_args = [vp] * 11 + [i, i, i, i, i, i, i, f]
+        L.attn_bwd_varlen.argtypes = bwdv_args + [vp]
+        L.attn_bwd_varlen.restype = i
+        L.attn_bwd_varlen_check.argtypes = bwdv_args
+        L.attn_bwd_varlen_check.restype = i
         fp8_args = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, f, f, f]
         L.attn_fwd_fp8.argtypes = fp8_args + [vp]
         L.attn_fwd_fp8.restype = i
@@ -408,3 +413,59 @@ def attention_fp8(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, scales, ca
     if st != ATTN_OK:
         raise AttnError(st, last_error())
     return out, lse
+
+
+def attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, delta, cu, B, H, Hkv, total, max_seqlen, d, causal, scale,
+                    stream) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return lib().attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, delta, cu, B, H, Hkv, total, max_seqlen, d,
+                                 int(causal), scale, stream)
+
+
+def attn_bwd_varlen_check(q, k, v, o, lse, dout, dq, dk, dv, delta, cu, B, H, Hkv, total, max_seqlen, d, causal,
+                          scale) -> int:
+    return lib().attn_bwd_varlen_check(q, k, v, o, lse, dout, dq, dk, dv, delta, cu, B, H, Hkv, total, max_seqlen,
+                                       d, int(causal), scale)
+
+
+def attention_backward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                              dout: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int | None = None,
+                              causal: bool = False, scale: float | None = None):
+    """Backward of packed variable-length attention on the current stream: returns (dQ, dK, dV, delta).
+
+    q, o, dout: bfloat16 [H,total,d]; k, v: bfloat16 [Hkv,total,d]; lse: float32 [H,total]
+    (o and lse from attention_varlen with the same cu_seqlens, causal flag and scale);
+    cu_seqlens: int32 [B+1] on the same device.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() \
+                or t.dim() != 3:
+            raise TypeError(f"{name} must be a contiguous bfloat16 3-d CUDA tensor")
+    H, T, d = q.shape
+    Hkv = k.shape[0]
+    if tuple(k.shape) != (Hkv, T, d) or tuple(v.shape) != (Hkv, T, d):
+        raise ValueError(f"k and v must be [Hkv,{T},{d}]")
+    if tuple(o.shape) != (H, T, d) or tuple(dout.shape) != (H, T, d):
+        raise ValueError(f"o and dout must be [{H},{T},{d}]")
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or tuple(lse.shape) != (H, T)
+            or not lse.is_contiguous() or lse.device != q.device):
+        raise TypeError("lse must be a contiguous float32 [H,total] tensor on q's device")
+    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous()):
+        raise TypeError("cu_seqlens must be a contiguous int32 [B+1] tensor on q's device")
+    B = cu_seqlens.numel() - 1
+    if B < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if B > 0 else 0
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), cu_seqlens.data_ptr(), B, H,
+                         Hkv, T, max_seqlen, d, causal, scale, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, last_error())
+    return dq, dk, dv, delta

@@ -54,10 +54,14 @@ struct BwdParams {
   __bf16* dk;         // [B][Hkv][N][D]
   __bf16* dv;         // [B][Hkv][N][D]
   float* delta;       // [B][H][N]: D_i = dO_i . O_i (written by the dq kernel)
-  int N;
+  // packed variable-length batches: every tensor is [heads][total][D] (lse, delta
+  // [H][total]) and sequence s owns tokens cu_seqlens[s] .. cu_seqlens[s+1]-1
+  const int* cu_seqlens;  // nseq + 1 cumulative lengths (device)
+  int nseq;
+  int N;              // dense: sequence length; packed: total tokens
   int H;
   int G;              // query heads per key/value head
-  int n_tiles;        // ceil(N / 128) row tiles per head
+  int n_tiles;        // ceil(N / 128) row tiles per head (packed: per longest sequence)
   float scale;
   float c;            // scale * log2(e)
 };
@@ -170,9 +174,17 @@ __device__ __forceinline__ void sync_tiles() {
   __syncthreads();
 }
 
+// Packed batches: the clamped bounds [a, e) of sequence s (the forward kernel's
+// reading: any contents of cu_seqlens stay inside [0, total]).
+__device__ __forceinline__ void seq_bounds(const BwdParams& p, int s, int& a, int& e) {
+  a = min(max(p.cu_seqlens[s], 0), p.N);
+  e = min(max(p.cu_seqlens[s + 1], a), p.N);
+}
+
 // ---------------------------------------------------------------------------
-// dq kernel: workgroup = (b, h, 128 query rows).
-template <int D, bool CAUSAL>
+// dq kernel: workgroup = (b, h, 128 query rows); packed batches (VARLEN):
+// workgroup = (h, sequence, 128 query rows of that sequence).
+template <int D, bool CAUSAL, bool VARLEN = false>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) {
   constexpr int KK = D / 16, MT = D / 32, NC = kTile / 32;
   constexpr int TB = kTile * D * 2;
@@ -187,20 +199,33 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
-  const int N = p.N;
-  const int bh = blockIdx.x / p.n_tiles;
-  const int i0 = (blockIdx.x - bh * p.n_tiles) * kRows;
-  const int b = bh / p.H, h = bh - b * p.H;
-  const int kvh = b * (p.H / p.G) + h / p.G;
-  const size_t qhead = (size_t)bh * N * D;
-  const size_t kvhead = (size_t)kvh * N * D;
+  const int hb = blockIdx.x / p.n_tiles;
+  const int i0 = (blockIdx.x - hb * p.n_tiles) * kRows;
+  int N;             // rows (and keys) of this workgroup's sequence
+  size_t qrow0, kvrow0;  // first row of the query head / key-value head in memory
+  if (VARLEN) {
+    const int h = hb / p.nseq, sq = hb - h * p.nseq;
+    int a, e;
+    seq_bounds(p, sq, a, e);
+    N = e - a;
+    if (i0 >= N) return;  // whole workgroup: past its sequence
+    qrow0 = (size_t)h * p.N + a;
+    kvrow0 = (size_t)(h / p.G) * p.N + a;
+  } else {
+    N = p.N;
+    const int b = hb / p.H, h = hb - b * p.H;
+    qrow0 = (size_t)hb * N;
+    kvrow0 = (size_t)(b * (p.H / p.G) + h / p.G) * N;
+  }
+  const size_t qhead = qrow0 * D;
+  const size_t kvhead = kvrow0 * D;
   const int my_q = i0 + 32 * wave + l32;
 
   bf16x8 qreg[KK], doreg[KK], oreg[KK];
   load_row_operand<D>(qreg, p.q + qhead, N, my_q, hl);
   load_row_operand<D>(doreg, p.dout + qhead, N, my_q, hl);
   load_row_operand<D>(oreg, p.o + qhead, N, my_q, hl);
-  const __amdgpu_buffer_rsrc_t lrs = rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t lrs = rsrc(p.lse + qrow0, (uint32_t)N * 4);
   const float lse2 =
       __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lrs, (uint32_t)my_q * 4, 0, 0)) * 1.44269504088896341f;
   float dpart = 0.f;
@@ -209,7 +234,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) 
 #pragma unroll
     for (int e = 0; e < 8; ++e) dpart = fmaf((float)doreg[kk][e], (float)oreg[kk][e], dpart);
   const float Di = pair_sum(dpart);
-  if (my_q < N && hl == 0) p.delta[(size_t)bh * N + my_q] = Di;
+  if (my_q < N && hl == 0) p.delta[qrow0 + my_q] = Di;
 
   const int kv_end = CAUSAL ? min(N, i0 + kRows) : N;
   const int n_kt = (kv_end + kTile - 1) / kTile;
@@ -264,13 +289,14 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) 
     step(t + 1, kt1, vt1, kt0, vt0);
   }
   if (t < n_kt) step(t, kt0, vt0, kt1, vt1);
-  if (my_q < N) store_rows<D>(p.dq, (size_t)bh * N + my_q, acc, p.scale, hl);
+  if (my_q < N) store_rows<D>(p.dq, qrow0 + my_q, acc, p.scale, hl);
 }
 
 // ---------------------------------------------------------------------------
 // dkdv kernel: workgroup = (b, key/value head g, 128 key rows); walks the query
-// tiles of query heads g*G .. g*G + G - 1.
-template <int D, bool CAUSAL>
+// tiles of query heads g*G .. g*G + G - 1. Packed batches (VARLEN): workgroup =
+// (g, sequence, 128 key rows of that sequence).
+template <int D, bool CAUSAL, bool VARLEN = false>
 __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(const BwdParams p) {
   constexpr int KK = D / 16, MT = D / 32, NC = kTile / 32;
   constexpr int TB = kTile * D * 2;
@@ -287,12 +313,30 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(co
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
-  const int N = p.N;
   const int Hkv = p.H / p.G;
-  const int bg = blockIdx.x / p.n_tiles;  // b * Hkv + g
+  const int bg = blockIdx.x / p.n_tiles;  // dense: b * Hkv + g; packed: g * nseq + sequence
   const int j0w = (blockIdx.x - bg * p.n_tiles) * kRows;
-  const int b = bg / Hkv, g = bg - b * Hkv;
-  const size_t kvhead = (size_t)bg * N * D;
+  int N, g;
+  size_t kvrow0, qrow_first, qrow_step;  // query head hq starts at row qrow_first + hq * qrow_step
+  if (VARLEN) {
+    g = bg / p.nseq;
+    const int sq = bg - g * p.nseq;
+    int a, e;
+    seq_bounds(p, sq, a, e);
+    N = e - a;
+    if (j0w >= N) return;  // whole workgroup: past its sequence
+    kvrow0 = (size_t)g * p.N + a;
+    qrow_first = a;
+    qrow_step = p.N;
+  } else {
+    N = p.N;
+    const int b = bg / Hkv;
+    g = bg - b * Hkv;
+    kvrow0 = (size_t)bg * N;
+    qrow_first = (size_t)b * p.H * N;
+    qrow_step = N;
+  }
+  const size_t kvhead = kvrow0 * D;
   const int my_k = j0w + 32 * wave + l32;
 
   bf16x8 kreg[KK], vreg[KK];
@@ -316,7 +360,7 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(co
     st = min(st, steps - 1);
     const int hq = g * p.G + st / per_head;
     const int iq0 = (it0 + st % per_head) * kTile;
-    const size_t qhead = ((size_t)b * p.H + hq) * N;
+    const size_t qhead = qrow_first + (size_t)hq * qrow_step;
     load_tile64<D>(p.q + qhead * D, N, iq0, Qb, wave, lane);
     load_tile64<D>(p.dout + qhead * D, N, iq0, dOb, wave, lane);
     if (wave == 0) load_vec64(p.lse + qhead, N, iq0, lb, lane);
@@ -377,8 +421,8 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(co
   }
   if (t < steps) step(t, qt0, dot0, lse0, del0, qt1, dot1, lse1, del1);
   if (my_k < N) {
-    store_rows<D>(p.dk, (size_t)bg * N + my_k, dka, p.scale, hl);
-    store_rows<D>(p.dv, (size_t)bg * N + my_k, dva, 1.f, hl);
+    store_rows<D>(p.dk, kvrow0 + my_k, dka, p.scale, hl);
+    store_rows<D>(p.dv, kvrow0 + my_k, dva, 1.f, hl);
   }
 }
 

@@ -55,6 +55,39 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
                        int Hkv, int N, int d, int causal, float scale, void* stream);
 
+/*
+ * attn_bwd_varlen - backward of packed variable-length attention (the layout of
+ * attn_fwd_varlen in attn_fwd.h: several sequences folded into the token axis).
+ *   q, o, dout, dq : bf16 [H][total][d]; k, v, dk, dv : bf16 [Hkv][total][d];
+ *   lse, delta     : fp32 [H][total]; o and lse from attn_fwd_varlen with the same
+ *                    cu_seqlens, causal flag and scale.
+ *   cu_seqlens     : DEVICE int32 [B+1] cumulative lengths (cu[0] = 0, cu[B] =
+ *                    total, non-decreasing), 4-byte aligned. Not validated (that
+ *                    would need a synchronisation): the kernels clamp every bound
+ *                    into [0, total], so no contents take an access outside the
+ *                    tensors; the results of an ill-formed array are undefined.
+ *   max_seqlen     : host int >= the longest sequence; it sizes the launch. Rows
+ *                    past ceil(max_seqlen / 128) * 128 of a longer sequence are
+ *                    not written.
+ * Each sequence is the backward pass of attn_bwd on its own rows and keys (the
+ * causal mask counts positions from the sequence's first token); dk and dv of a
+ * shared key/value head are summed over its query heads. Same error codes as
+ * attn_bwd (ATTN_ERR_NULL also for cu_seqlens; ATTN_ERR_DIM for negative
+ * max_seqlen or total); B*H*min(max_seqlen, total) == 0 returns ATTN_OK and
+ * launches nothing.
+ */
+attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              float* delta, const int* cu_seqlens, int B, int H, int Hkv, int total,
+                              int max_seqlen, int d, int causal, float scale, void* stream);
+
+/* Host-only argument check of attn_bwd_varlen (never touches the device). */
+attn_status_t attn_bwd_varlen_check(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const void* dout, const void* dq,
+                                    const void* dk, const void* dv, const float* delta,
+                                    const int* cu_seqlens, int B, int H, int Hkv, int total,
+                                    int max_seqlen, int d, int causal, float scale);
+
 /* Host-only argument check of attn_bwd (never touches the device). */
 attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dout, const void* dq, const void* dk,

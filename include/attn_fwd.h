@@ -48,8 +48,9 @@ extern "C" {
  * 3: adds attn_fwd_varlen and attn_fwd_varlen_check (packed variable-length batches).
  * 4: adds attn_bwd and attn_bwd_check (backward pass, declared in attn_bwd.h).
  * 5: adds attn_fwd_splitkv and attn_fwd_splitkv_workspace_size (split keys).
- * 6: adds attn_fwd_fp8 and attn_fwd_fp8_check (FP8 e4m3 inputs, declared in attn_fp8.h). */
-#define ATTN_ABI_VERSION 6
+ * 6: adds attn_fwd_fp8 and attn_fwd_fp8_check (FP8 e4m3 inputs, declared in attn_fp8.h).
+ * 7: adds attn_bwd_varlen and attn_bwd_varlen_check (declared in attn_bwd.h). */
+#define ATTN_ABI_VERSION 7
 
 typedef enum attn_status {
   ATTN_OK = 0,

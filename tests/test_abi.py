@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(bnd.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.attn_abi_version() == bnd.ABI_VERSION == 6
+    assert lib.attn_abi_version() == bnd.ABI_VERSION == 7
 
 
 def check(*args, **kw):
@@ -300,3 +300,28 @@ def test_fp8_alias_uses_transposed_padded_extent():
     assert ldv == 8208
     assert fp8_check(B=B, H=H, N=N, d=d, lse=V + d * ldv - 16) == 6
     assert fp8_check(B=B, H=H, N=N, d=d, lse=V + d * ldv) == bnd.ATTN_OK
+
+
+CU = 12 * GB
+
+
+def test_bwd_varlen_valid_and_empty():
+    # (q, k, v, o, lse, dout, dq, dk, dv, delta, cu, B, H, Hkv, total, max_seqlen, d, causal, scale)
+    ok = [Q, K, V, O, L, DO, DQ, DK, DV, DL, CU, 24, 32, 8, 42747, 5753, 128, 1, 0.088]
+    assert bnd.attn_bwd_varlen_check(*ok) == bnd.ATTN_OK
+    assert bnd.attn_bwd_varlen_check(*([None] * 11), 0, 4, 2, 16, 16, 64, 0, 1.0) == bnd.ATTN_OK
+    assert bnd.attn_bwd_varlen_check(*([None] * 11), 3, 4, 2, 16, 0, 64, 0, 1.0) == bnd.ATTN_OK
+    assert bnd.attn_bwd_varlen(*([None] * 11), 3, 4, 2, 0, 8, 64, 0, 1.0, None) == bnd.ATTN_OK
+
+
+@pytest.mark.parametrize("patch,code", [
+    ({10: None}, 1), ({0: None}, 1), ({14: -1}, 2), ({15: -1}, 2), ({13: 3}, 2), ({14: 1 << 24}, 2),
+    ({16: 80}, 3), ({18: math.nan}, 5), ({10: CU + 2}, 4), ({6: DQ + 8}, 4), ({9: CU}, 6), ({7: DQ + 64}, 6),
+])
+def test_bwd_varlen_error_codes(patch, code):
+    args = [Q, K, V, O, L, DO, DQ, DK, DV, DL, CU, 3, 4, 2, 500, 300, 64, 1, 1.0]
+    for i, x in patch.items():
+        args[i] = x
+    assert bnd.attn_bwd_varlen_check(*args) == code
+    assert bnd.last_error() != ""
+    assert bnd.attn_bwd_varlen(*args, None) == code
