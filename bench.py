@@ -193,6 +193,38 @@ def time_split(w, steps, warmup):
     return ms
 
 
+def time_backward_varlen(w, steps, warmup):
+    """Average time (ms) of one attn_bwd_varlen call on a packed workload (O and LSE from one
+    attn_fwd_varlen pass; dO drawn N(0,1))."""
+    import torch
+
+    from exact_attention_22_amd import binding
+
+    dev = torch.device("cuda:0")
+    q, k, v, cu = (t.to(dev) for t in w.inputs())
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 7919)
+    do = torch.randn(q.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
+    mx = max(w.lengths)
+    o, lse = binding.attention_varlen(q, k, v, cu, max_seqlen=mx, causal=w.causal, scale=w.scale)
+
+    def call():
+        binding.attention_backward_varlen(q, k, v, o, lse, do, cu, max_seqlen=mx, causal=w.causal, scale=w.scale)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del q, k, v, cu, do, o, lse
+    torch.cuda.empty_cache()
+    return ms
+
+
 def time_fp8(w, steps, warmup):
     """Average time (ms) of attn_fwd_fp8 on a dense workload's shape: the same N(0,1)
     draws quantised to e4m3 with per-tensor scales, V transposed."""
@@ -377,6 +409,11 @@ def main():
             bt = 2.5 * o.flops / (bms * 1e-3) / 1e12
             backward[name] = {"ms": round(bms, 4), "tflops": round(bt, 1), "frac_peak": round(bt / PEAK_BF16_TFLOPS, 4),
                               "causal": o.causal, "shape": describe(o)}
+        vw = inputs.VARLEN
+        bms = time_backward_varlen(vw, max(5, args.steps // 5), 3)
+        bt = 2.5 * vw.flops / (bms * 1e-3) / 1e12
+        backward[vw.name] = {"ms": round(bms, 4), "tflops": round(bt, 1), "frac_peak": round(bt / PEAK_BF16_TFLOPS, 4),
+                             "causal": vw.causal, "shape": describe(vw)}
 
     splitkv = {}
     if not args.no_others:  # split keys on shapes with fewer query tiles than compute units
