@@ -17,7 +17,10 @@ import hashlib
 import json
 import math
 import os
+import re
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -256,6 +259,33 @@ def time_fp8(w, steps, warmup):
     return ms
 
 
+class ClockSampler(threading.Thread):
+    """Reads the GPU's current SCLK with rocm-smi (a child process) about every 0.3 s while
+    the timed samples run; values in MHz, empty if rocm-smi is absent or prints no clock."""
+
+    def __init__(self):
+        super().__init__(daemon=True)
+        self.mhz = []
+        self.done = threading.Event()
+
+    def run(self):
+        while not self.done.is_set():
+            try:
+                out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            self.mhz += [int(m.group(1)) for m in re.finditer(r"sclk[^\n]*?\((\d+)\s*mhz\)", out, re.I)]
+            self.done.wait(0.3)
+
+    def summary(self):
+        self.done.set()
+        self.join(timeout=15)
+        if not self.mhz:
+            return None
+        v = sorted(self.mhz)
+        return {"n": len(v), "median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1]}
+
+
 def time_samples(w, n_samples=20, min_ms=50.0):
     """n_samples timed batches of back-to-back launches, each at least min_ms long;
     per-launch median and min (ms)."""
@@ -379,7 +409,10 @@ def main():
     tflops = w.flops / (ms * 1e-3) / 1e12
     samples = None
     if not args.no_others:  # 20 batches of >= 50 ms of back-to-back launches: median and min
+        clock = ClockSampler()
+        clock.start()
         samples = time_samples(w)
+        samples["sclk"] = clock.summary()
         samples["median_tflops"] = round(w.flops / (samples["median_ms"] * 1e-3) / 1e12, 1)
         samples["max_tflops"] = round(w.flops / (samples["min_ms"] * 1e-3) / 1e12, 1)
 
