@@ -129,3 +129,23 @@ def test_fp8_wrapper_rejects_bad_arguments():
         binding.attention_fp8(q, k, vt, sc, tau=9.0)
     with pytest.raises(binding.AttnError):
         binding.attention_fp8(q, k, vt, (0.0, 1.0, 1.0))
+
+
+def test_fp8_wide_range_codes_stay_within_dot_product_bound():
+    """Q and K codes drawn uniformly over every finite e4m3 value (magnitudes 2^-9 .. 448, the
+    worst case for the alignment inside the matrix instruction): the LSE error must stay within
+    the score bound E = 2^-10 * scale * max_j sum_k |q_k k_k| that the oracle assumes for the
+    matrix core's e4m3 dot products, and O within its per-row bound."""
+    B, H, N, d = 1, 2, 384, 128
+    g = torch.Generator().manual_seed(123)
+    codes = torch.randint(0, 256, (3, B, H, N, d), generator=g, dtype=torch.int32).to(torch.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38      # NaN patterns -> 1.0
+    q8, k8, v8 = codes[0].contiguous(), codes[1].contiguous(), codes[2]
+    vt8 = torch.zeros((B, H, d, inputs.fp8_ldv(N)), dtype=torch.uint8)
+    vt8[..., :N] = v8.transpose(-1, -2)
+    sc = (1.0 / 448, 1.0 / 448, 1.0 / 448)
+    for causal in (False, True):
+        o, lse = run_fp8(q8, k8, vt8, sc, causal, 0.5)
+        o_ref, lse_ref = of.attention_fp8(q8, k8, vt8, sc, causal, 0.5)
+        bo, bl = of.fp8_error_bound(q8, k8, vt8, sc, causal, 0.5)
+        check_rows(o, lse, o_ref, lse_ref, bo, bl, f"wide-range codes causal={causal}")
