@@ -29,19 +29,40 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
+SOURCES = ("attn_fwd.hip", "attn_bwd.hip", "attn_fp8.hip")
+
+
 def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Always recompiles; returns the path of the shared library."""
+    """Always recompiles; returns the path of the shared library.
+
+    Each translation unit is compiled to an object in parallel, then linked."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", *HIP_FLAGS, "-shared",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_bwd.hip"),
-           os.path.join(CSRC, "attn_fp8.hip"), "-o", tmp, *(extra or [])]
+    objs = [f"{out}.{os.path.splitext(src)[0]}.o" for src in SOURCES]
+    base = [hipcc(), f"--offload-arch={ARCH}", *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    procs = []
+    for src, obj in zip(SOURCES, objs):
+        cmd = [*base, "-c", os.path.join(CSRC, src), "-o", obj, *(extra or [])]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+    failed = False
+    for p in procs:
+        text, _ = p.communicate()
+        if p.returncode != 0:
+            sys.stderr.write(text)
+            failed = True
+    if failed:
+        raise RuntimeError("hipcc failed")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
+    for obj in objs:
+        if os.path.exists(obj):
+            os.remove(obj)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(tmp, out)
     return out
 

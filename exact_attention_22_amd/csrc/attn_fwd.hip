@@ -238,6 +238,7 @@ attn_status_t run(const Problem& P, int causal, const attn_fwd_opts* opts, void*
   p.c = P.scale * 1.44269504088896341f;
   if (p.c == 0.f) p.c = 0x1p-100f;
   p.tau = o2.rescale_tau_log2;
+  p.psum_thr = (1.f - 0x1p-10f) * exp2f(o2.rescale_tau_log2);  // P above 2^tau puts a partial sum above this
   p.n_splits = 1;
   p.split_tiles = 0;
   p.ws_o = nullptr;
@@ -323,6 +324,7 @@ attn_status_t run_split(const Problem& P, int causal, int n_splits, void* ws, si
   p.c = P.scale * 1.44269504088896341f;
   if (p.c == 0.f) p.c = 0x1p-100f;
   p.tau = o2.rescale_tau_log2;
+  p.psum_thr = (1.f - 0x1p-10f) * exp2f(o2.rescale_tau_log2);  // P above 2^tau puts a partial sum above this
   p.n_splits = splits;
   p.split_tiles = split_tiles;
   p.ws_o = (float*)ws;

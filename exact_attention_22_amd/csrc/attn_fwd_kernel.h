@@ -91,6 +91,7 @@ struct Params {
   int per_xcd;         // ceil(total_tiles / 8): workgroups per XCD slice
   float c;             // scale * log2(e) in fp32; +-2^-100 stands in for 0 (see the launcher)
   float tau;           // rescale threshold, log2 units
+  float psum_thr;      // 2^tau * (1 - 2^-10): partial tile sums above it take the exact-maximum path
   // split keys: tile (bh, qt) is n_splits units, unit s covering key tiles
   // [s * split_tiles, (s + 1) * split_tiles); each writes its normalised O and LSE
   // over those keys to ws_o [n_splits][B*H*N][D] and ws_lse [n_splits][B*H*N]
@@ -253,6 +254,7 @@ struct RowState {
   f32x16 oacc[D / 32];  // O^T accumulator (unnormalised)
   float m_used;          // maximum in use, log2 units
   float thr;             // m_used + tau: a tile maximum above it triggers a rescale
+  float psum_thr;        // 2^tau less a margin: a tile's partial sum above it may need a rescale
   float l_sum;           // this lane's partial row sum
   int n_rescale;
 };
@@ -303,9 +305,11 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 
   constexpr int MT = D / 32;
   constexpr float mask_val = NEG ? INFINITY : -INFINITY;
   const int hl = lane >> 5;
-  // This tile's PV operands (V_t^T) are read from LDS now, so their latency
-  // hides under the exponentials; the matrix phase finds them in registers.
-  v_read<D, BC, 0, 2 * NC>(va, vb, voffs);
+  // This tile's PV operands (V_t^T) are read from LDS in this phase, so their
+  // latency hides under the exponentials and the matrix phase finds them in
+  // registers: the first half now, the second half once the scores are dead
+  // (the scores stay live until the rescale check after the exponentials).
+  v_read<D, BC, 0, NC>(va, vb, voffs);
   if (masked) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
@@ -316,42 +320,61 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 
         s[cc][r] = hide ? mask_val : s[cc][r];
       }
   }
-  float red = s[0][0];
+  // P = 2^(s*c - m) with the maximum in use m, and this lane's partial sum of the
+  // tile. Two partial sums keep the additions off one dependency chain.
+  auto exponentials = [&](float mc) -> float {
+    float part[2] = {0.f, 0.f};
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc)
+    for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red = NEG ? fminf(red, s[cc][r]) : fmaxf(red, s[cc][r]);
-  red = NEG ? pair_min(red) : pair_max(red);
-  const float m_tile = red * c;  // -inf when every key of the row is masked (c is never 0)
-  const bool need = m_tile > st.thr;
-  if (__any(need)) {
-    const float alpha = need ? __builtin_amdgcn_exp2f(st.m_used - m_tile) : 1.f;
-    st.n_rescale += (need && st.m_used != -INFINITY) ? 1 : 0;
-    st.m_used = need ? m_tile : st.m_used;
-    st.thr = st.m_used + tau;
-    st.l_sum *= alpha;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int j = 0; j < 8; ++j) {
+          const int r = 8 * h + j;
+          const float x = fmaf(s[cc][r], c, mc);
+          float e;
+          if (POLY8 == 8 || (POLY8 == 4 && (r & 4)))
+            e = attn_exp2_poly(x);
+          else
+            e = __builtin_amdgcn_exp2f(x);
+          part[j & 1] += e;
+          pb[cc][h][j] = (__bf16)e;
+        }
+    return part[0] + part[1];
+  };
+  // The tile maximum is needed only when a rescale may be due: a row whose
+  // tile maximum exceeds m + tau has a P above 2^tau, so the partial sum of the
+  // lane holding that key exceeds 2^tau (the sum of non-negative terms is at
+  // least each term). The exponentials are therefore taken with the maximum in
+  // use first, and only a wavefront with such a sum (or with m still -inf,
+  // which gives +inf or NaN) computes the exact tile maximum, applies the
+  // threshold rule per row and takes the exponentials again. The rescale policy
+  // is unchanged; its maximum reduction leaves the common path.
+  float tsum = exponentials(-st.m_used);
+  if (__any(!(tsum <= st.psum_thr))) {
+    float red = s[0][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st.oacc[mt][r] *= alpha;
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red = NEG ? fminf(red, s[cc][r]) : fmaxf(red, s[cc][r]);
+    red = NEG ? pair_min(red) : pair_max(red);
+    const float m_tile = red * c;  // -inf when every key of the row is masked (c is never 0)
+    const bool need = m_tile > st.thr;
+    if (__any(need)) {  // otherwise the exponentials above stand
+      const float alpha = need ? __builtin_amdgcn_exp2f(st.m_used - m_tile) : 1.f;
+      st.n_rescale += (need && st.m_used != -INFINITY) ? 1 : 0;
+      st.m_used = need ? m_tile : st.m_used;
+      st.thr = st.m_used + tau;
+      st.l_sum *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.oacc[mt][r] *= alpha;
+      tsum = exponentials(-st.m_used);
+    }
   }
-  const float mc = -st.m_used;
-#pragma unroll
-  for (int cc = 0; cc < NC; ++cc)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 8 * h + j;
-        const float x = fmaf(s[cc][r], c, mc);
-        float e;
-        if (POLY8 == 8 || (POLY8 == 4 && (r & 4)))
-          e = attn_exp2_poly(x);
-        else
-          e = __builtin_amdgcn_exp2f(x);
-        st.l_sum += e;
-        pb[cc][h][j] = (__bf16)e;
-      }
+  st.l_sum += tsum;
+  v_read<D, BC, NC, 2 * NC>(va, vb, voffs);
   // P is consumed only after the phase barrier and the row sum only at the next
   // rescale; these empty asm uses keep both computed in this phase instead of
   // letting them sink past the barrier (which would keep the fp32 exponentials
@@ -570,6 +593,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   for (int mt = 0; mt < MT; ++mt) st.oacc[mt] = f32x16{};
   st.m_used = -INFINITY;
   st.thr = -INFINITY;
+  st.psum_thr = p.psum_thr;
   st.l_sum = 0.f;
   st.n_rescale = 0;
 
