@@ -31,10 +31,14 @@
 //
 // Data movement: K and V tiles go from HBM/L2 straight into LDS with buffer
 // loads that write LDS (each wave instruction fills 1 KiB: lane l's 16 bytes
-// land at base + 16*l), double-buffered. Rows are stored
-// unpadded with an XOR swizzle of their 16-byte chunks, chosen so that both the
-// 16-byte K reads and the V transpose reads are free of bank conflicts. Keys
-// past N read as zeros (buffer range check) and are masked.
+// land at base + 16*l), double-buffered (V as a head and a tail, see VSplit).
+// Rows are stored unpadded with an XOR swizzle of their 16-byte chunks, chosen
+// so that both the 16-byte K reads and the V transpose reads are free of bank
+// conflicts. Keys past N read as zeros (buffer range check) and are masked.
+// Every LDS read is issued by the wavefront in its matrix phase, under its own
+// products: on gfx950 an LDS read occupies the issuing wavefront for about
+// (bytes / 64) cycles but does not slow a matrix-core wavefront on the same
+// SIMD, so reads in the softmax phase would lengthen the critical path.
 //
 // Schedule: a workgroup holds two groups of four wavefronts (one of each per
 // SIMD) that alternate, one phase apart, between the softmax of tile t on the
@@ -151,13 +155,15 @@ __device__ __forceinline__ uint32_t load_offset(int wave, int lane) {
   return (uint32_t)(r * D + 8 * c) * 2;
 }
 
-// A tile that is not `live` (past the last tile) gets zero-size resources: its
-// loads fill the buffer with zeros without touching memory, so every step issues
-// the same loads and the load/wait sequence has no branches.
+// A tile that is not `live` (past the last tile, or starting at or past row N)
+// gets zero-size resources: its loads fill the buffer with zeros without touching
+// memory, so every step issues the same loads and the load/wait sequence has no
+// branches.
 template <int D, int BC, int NW>
 __device__ __forceinline__ void load_tile(uint32_t off, const __bf16* head, int N, int j0, char* buf, int wave,
                                           bool live) {
   using S = LoadShape<D, BC, NW>;
+  live = live && j0 < N;  // a half tile can start past the last key
   const char* base = (const char*)(head + (size_t)(live ? j0 : 0) * D);
   const uint32_t bytes = live ? (uint32_t)(N - j0) * D * 2 : 0u;
 #pragma unroll
@@ -268,17 +274,16 @@ struct RowState {
 // round-robin, so every SIMD holds one wavefront of each group and always has
 // one of them feeding the matrix core while the other runs the softmax.
 //
-// Global step 2k:   A: softmax(k)          B: loads V_{k+1}; matrix(k-1)
-// Global step 2k+1: A: matrix(k)           B: loads K_{k+2}; softmax(k)
+// Global step 2k:   A: softmax(k)                 B: loads V_{k+1}; matrix(k-1)
+// Global step 2k+1: A: loads K_{k+2}; matrix(k)   B: softmax(k)
 // Each group runs pairs (softmax(k), matrix(k)), so the PV operands and P of a
 // tile live within one pair; group B starts with a step that only loads and
 // group A ends with an empty step, which keeps their barrier counts equal.
 // The softmax phase of tile t also reads V_t's PV operands from LDS, so V_t
-// must be resident one step before its product. Group B issues every tile load
-// at the start of a step and waits for the previous step's loads at its end,
-// before the barrier; a tile issued at step s is therefore visible from step
-// s + 2, and its buffer was last read at step s - 1. Group A never has loads of
-// its own in flight.
+// must be resident one step before its product. Each group issues its tile
+// loads at the start of its matrix phase and waits for them at the end of its
+// next softmax phase, before the barrier; a tile issued at step s is therefore
+// visible from step s + 2, and its buffer was last read at step s - 1.
 // ============================================================================
 
 // Barrier between phases. It waits for this wavefront's LDS reads and writes
@@ -294,22 +299,17 @@ __device__ __forceinline__ void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// VALU phase: mask (boundary tiles), tile maximum, adaptive rescale,
-// P = 2^(s*c - m) with the fp32 row sum, packed to bf16 in the PV operand order.
+// VALU phase: mask (boundary tiles), adaptive rescale, P = 2^(s*c - m) with the
+// fp32 row sum, packed to bf16 in the PV operand order. The phase issues no LDS
+// reads: an LDS read holds its own wavefront's issue for about (bytes / 64)
+// cycles, which the matrix phase hides under its products and this phase cannot.
 template <int D, int BC, bool CAUSAL, int POLY8, bool NEG>
 __device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 32][2],
-                                              bf16x8 (&va)[BC / 32][2][D / 32], const char* vb,
-                                              const int (&voffs)[D / 32], bool masked, int j0, int N, int my_q,
-                                              int lane, float c, float tau) {
+                                              bool masked, int j0, int N, int my_q, int lane, float c, float tau) {
   constexpr int NC = BC / 32;
   constexpr int MT = D / 32;
   constexpr float mask_val = NEG ? INFINITY : -INFINITY;
   const int hl = lane >> 5;
-  // This tile's PV operands (V_t^T) are read from LDS in this phase, so their
-  // latency hides under the exponentials and the matrix phase finds them in
-  // registers: the first half now, the second half once the scores are dead
-  // (the scores stay live until the rescale check after the exponentials).
-  v_read<D, BC, 0, NC>(va, vb, voffs);
   if (masked) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
@@ -340,6 +340,12 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 
           part[j & 1] += e;
           pb[cc][h][j] = (__bf16)e;
         }
+    // pack here: otherwise the packing sinks past the rescale check below and
+    // keeps every fp32 exponential live until then
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(pb[cc][h]));
     return part[0] + part[1];
   };
   // The tile maximum is needed only when a rescale may be due: a row whose
@@ -374,7 +380,6 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 
     }
   }
   st.l_sum += tsum;
-  v_read<D, BC, NC, 2 * NC>(va, vb, voffs);
   // P is consumed only after the phase barrier and the row sum only at the next
   // rescale; these empty asm uses keep both computed in this phase instead of
   // letting them sink past the barrier (which would keep the fp32 exponentials
@@ -386,44 +391,104 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 
   asm volatile("" : "+v"(st.l_sum));
 }
 
-// Matrix phase: O^T += V_t^T P_t^T with the V operands already in registers,
-// then S = K_{t+1} Q^T with K_{t+1} in kb. The K fragment reads are issued one
-// per PV product, so they land while the matrix core works and take the
-// registers of the V operands already consumed. After a wavefront's last tile
-// kb holds stale keys; that S is never used.
-template <int D, int BC>
+// V tiles are stored as a head (the first VHK k-steps of 16 keys: 4 PV operands
+// per lane) and a tail (the other keys), each in its own double buffer. The head
+// of a tile is read one matrix phase ahead and carried in registers, so the
+// first PV products of a matrix phase never wait for LDS; the tail is read
+// during the same phase's products, one k-step ahead of its use.
+template <int D>
+struct VSplit {
+  static constexpr int MT = D / 32;
+  static constexpr int HKS = 4 / MT;       // head k-steps (4 operands per lane)
+  static constexpr int HROWS = 16 * HKS;   // head keys
+  static_assert(4 % MT == 0, "head of whole k-steps");
+};
+
+// Number of LDS reads issued after PV product (g, mt) of matrix_phase.
+template <int D, int BC, int KA>
+__host__ __device__ constexpr int pv_reads(int g, int mt) {
+  constexpr int NKS = BC / 16, HKS = VSplit<D>::HKS;
+  return 2 * (g + 1 >= HKS && g + 1 < NKS) + 2 * (g >= NKS - HKS) + (g == NKS - 1 && mt < KA);
+}
+template <int D, int BC, int KA, int I>
+__device__ __forceinline__ void pv_sched() {
+  constexpr int MT = D / 32, NPV = (BC / 16) * MT;
+  if constexpr (I < NPV) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, pv_reads<D, BC, KA>(I / MT, I % MT), 0);
+    pv_sched<D, BC, KA, I + 1>();
+  }
+}
+
+// Matrix phase: O^T += V_t^T P_t^T, then S_{t+1} = K_{t+1} Q^T. V_t's head
+// operands come in `va`; the LDS reads of this phase ride under the products:
+// after PV product (g, mt), the transpose reads of V_t's tail operand (g+1, mt)
+// (from `vtl`) or, in the last VHK k-steps, of V_{t+1}'s head operand (from
+// `vhd_next`, into `va` for the next matrix phase), and the first KA K_{t+1}
+// fragments after the last k-step's products; each QK product is followed by
+// the K fragment KA ahead. `loads` issues this wavefront's tile loads (if any),
+// one per product in the second half of the QK products. After a wavefront's
+// last tile the buffers hold stale data; that S and those operands are never
+// used.
+template <int D, int BC, int NLOADS, typename Loads>
 __device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 32], const bf16x8 (&pb)[BC / 32][2],
-                                             const bf16x8 (&va)[BC / 32][2][D / 32], const bf16x8 (&qreg)[D / 16],
-                                             const char* kb, int lane) {
+                                             bf16x8 (&va)[VSplit<D>::HKS][D / 32], const bf16x8 (&qreg)[D / 16],
+                                             const char* kb, const char* vtl, const char* vhd_next,
+                                             const int (&voffs)[D / 32], int lane, Loads&& loads) {
   constexpr int NC = BC / 32;
   constexpr int MT = D / 32;
   constexpr int KK = D / 16;
-  constexpr int NPV = NC * 2 * MT;  // PV products
+  constexpr int NKS = BC / 16;      // k-steps of 16 keys
+  constexpr int HKS = VSplit<D>::HKS;
   constexpr int NQK = NC * KK;      // QK products
-  static_assert(NQK == NPV, "one K fragment read per PV product");
+  constexpr int KA = MT < 4 ? MT : 4;  // K fragments read ahead of the QK products
+  static_assert(NLOADS <= NQK - KA, "one tile load per late QK product");
   const int l32 = lane & 31, hl = lane >> 5;
   // Issue priority up while this wavefront feeds the matrix core, so the
   // softmax wavefront on the same SIMD does not delay its MFMA issue.
   __builtin_amdgcn_s_setprio(1);
   bf16x8 kf[NQK];
+  bf16x8 vf[NKS][MT];
+  auto vfrag = [&](const char* buf, int ks, int mt) {  // ks: k-step within the buffer
+    const s16x4 lo = v_col4<D>(buf + voffs[mt], 16 * ks);
+    const s16x4 hi = v_col4<D>(buf + voffs[mt], 16 * ks + 8);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto kread = [&](int f) { kf[f] = k_frag<D>(kb, 32 * (f / KK) + l32, 2 * (f % KK) + hl); };
 #pragma unroll
-  for (int i = 0; i < NPV; ++i) {
-    const int cc = i / (2 * MT), h = (i / MT) % 2, mt = i % MT;
-    st.oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][h][mt], pb[cc][h], st.oacc[mt], 0, 0, 0);
-    kf[i] = k_frag<D>(kb, 32 * (i / KK) + l32, 2 * (i % KK) + hl);
-  }
+  for (int g = 0; g < HKS; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) vf[g][mt] = va[g][mt];
+#pragma unroll
+  for (int g = 0; g < NKS; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      st.oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g][mt], pb[g / 2][g % 2], st.oacc[mt], 0, 0, 0);
+      if (g + 1 >= HKS && g + 1 < NKS) vf[g + 1][mt] = vfrag(vtl, g + 1 - HKS, mt);
+      if (g >= NKS - HKS) va[g - (NKS - HKS)][mt] = vfrag(vhd_next, g - (NKS - HKS), mt);
+      if (g == NKS - 1 && mt < KA) kread(mt);
+    }
 #pragma unroll
   for (int f = 0; f < NQK; ++f) {
     const int cc = f / KK, kk = f % KK;
+    if (f + KA < NQK) kread(f + KA);
     s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[f], qreg[kk], kk == 0 ? f32x16{} : s[cc], 0, 0, 0);
   }
-  // Instruction order: PV products each followed by one K read, then the QK products.
+  loads();
+  // Instruction order as described above.
+  pv_sched<D, BC, KA, 0>();
 #pragma unroll
-  for (int i = 0; i < NPV; ++i) {
+  for (int f = 0; f < NQK - KA - NLOADS; ++f) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, NQK, 0);
+#pragma unroll
+  for (int f = 0; f < NLOADS; ++f) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, KA, 0);
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -444,10 +509,16 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert(!SPLIT || (OF32 && !VARLEN), "split keys: fp32 partials, dense layout");
 
+  // K tiles double-buffered; V tiles as head and tail, each double-buffered (they
+  // are read at different steps, see below)
+  constexpr int VHR = VSplit<D>::HROWS;  // head keys
+  constexpr int VTR = BC - VHR;          // tail keys
   __shared__ __attribute__((aligned(1024))) char kbuf0[TILEB];
   __shared__ __attribute__((aligned(1024))) char kbuf1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char vbuf0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vhd0[VHR * D * 2];
+  __shared__ __attribute__((aligned(1024))) char vhd1[VHR * D * 2];
+  __shared__ __attribute__((aligned(1024))) char vtl0[VTR * D * 2];
+  __shared__ __attribute__((aligned(1024))) char vtl1[VTR * D * 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -457,9 +528,9 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   const int hl = lane >> 5;
   const int N = p.N;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  constexpr int LPW = LoadShape<D, BC, 4>::LPW;  // group B's four wavefronts load every tile
   const uint32_t koff = load_offset<D, BC, 4, true>(wave & 3, lane);
-  const uint32_t voff = load_offset<D, BC, 4, false>(wave & 3, lane);
+  const uint32_t vhoff = load_offset<D, VHR, 4, false>(wave & 3, lane);
+  const uint32_t vtoff = load_offset<D, VTR, 4, false>(wave & 3, lane);
   int voffs[MT];
   v_offsets<D>(voffs, lane);
   const float c = p.c;
@@ -552,10 +623,14 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     // split keys: K and V start at the unit's first key tile
     const size_t kvoff = kvhead + (SPLIT ? (size_t)t.kb * BC * D : 0);
     const int nkv = n - (SPLIT ? t.kb * BC : 0);
-    if (grp == 1) {  // n_tiles >= 1
+    // K_0, K_1 (group A) and V_0, V_1's head (group B); n_tiles >= 1
+    if (grp == 0) {
       load_tile<D, BC, 4>(koff, p.k + kvoff, nkv, 0, kbuf0, wave & 3, true);
-      load_tile<D, BC, 4>(voff, p.v + kvoff, nkv, 0, vbuf0, wave & 3, true);
       load_tile<D, BC, 4>(koff, p.k + kvoff, nkv, BC, kbuf1, wave & 3, t.n_tiles > 1);
+    } else {
+      load_tile<D, VHR, 4>(vhoff, p.v + kvoff, nkv, 0, vhd0, wave & 3, true);
+      load_tile<D, VTR, 4>(vtoff, p.v + kvoff, nkv, VHR, vtl0, wave & 3, true);
+      load_tile<D, VHR, 4>(vhoff, p.v + kvoff, nkv, BC, vhd1, wave & 3, t.n_tiles > 1);
     }
     const __amdgpu_buffer_rsrc_t qrsrc =
         buffer_rsrc(p.q + head, VARLEN ? (uint32_t)n * D * 2 : head_bytes);
@@ -598,61 +673,74 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   st.n_rescale = 0;
 
   f32x16 s[NC];
+  bf16x8 va[VSplit<D>::HKS][MT];  // PV operands of the head of the V tile the next matrix phase multiplies
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's tile and Q loads landed
-  __syncthreads();                      // K_0, V_0, K_1 resident for every wavefront
+  __syncthreads();                      // K_0, K_1, V_0, V_1's head resident for every wavefront
+#pragma unroll
+  for (int g = 0; g < VSplit<D>::HKS; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const s16x4 lo = v_col4<D>(vhd0 + voffs[mt], 16 * g);
+      const s16x4 hi = v_col4<D>(vhd0 + voffs[mt], 16 * g + 8);
+      va[g][mt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, s, l32, hl);
 
   // Every wavefront runs all n_tiles tiles of its workgroup: a tile past a causal
   // row's last visible key is fully masked (P = 0) and leaves m, l and O as they
   // are, so no wavefront takes a separate code path. Tile k's buffers are
-  // kbuf/vbuf[k % 2]. Both groups pass 2 * n_tiles + 1 barriers.
+  // kbuf[k % 2], vhd[k % 2] and vtl[k % 2]. Both groups pass 2 * n_tiles + 1
+  // barriers.
+  //
+  // LDS reads: matrix(k) (group A at step 2k+1, group B at step 2k+2) reads
+  // V_k's tail, K_{k+1} and V_{k+1}'s head; the softmax phase reads none.
+  // Tile loads: group A issues, during matrix(k) (step 2k+1), K_{k+2} into
+  // kbuf[k % 2] and V_{k+2}'s head into vhd[k % 2] (K_k and V_k's head were last
+  // read by matrix(k-1), steps 2k-1 and 2k), and V_{k+1}'s tail into
+  // vtl[(k+1) % 2] (V_{k-1}'s tail was last read by matrix(k-1)). It waits for
+  // them at the end of softmax(k+1), before the barrier ending step 2k+2; all
+  // three are first read at step 2k+3. Every barrier waits for the wavefront's
+  // own LDS reads, so no buffer is overwritten under a read.
+  auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  constexpr int NLD =
+      LoadShape<D, BC, 4>::LPW + LoadShape<D, VHR, 4>::LPW + LoadShape<D, VTR, 4>::LPW;  // group A's loads per step
   if (grp == 0) {
-    auto pair = [&](int k, char* kb1, char* vb0) {
+    auto pair = [&](int k, char* kb0, char* kb1, char* vh0, char* vh1, char* vt0, char* vt1) {
       bf16x8 pb[NC][2];
-      bf16x8 va[NC][2][MT];
-      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, va, vb0, voffs, k >= t_full, (k + kt0) * BC, N, my_q, lane,
-                                               c, tau);
+      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau);
+      wait_loads();
       phase_barrier();
-      matrix_phase<D, BC>(st, s, pb, va, qreg, kb1, lane);
+      matrix_phase<D, BC, NLD>(st, s, pb, va, qreg, kb1, vt0, vh1, voffs, lane, [&] {
+        load_tile<D, BC, 4>(koff, kh, Nkv, (k + 2) * BC, kb0, wave & 3, k + 2 < n_tiles);
+        load_tile<D, VHR, 4>(vhoff, vh, Nkv, (k + 2) * BC, vh0, wave & 3, k + 2 < n_tiles);
+        load_tile<D, VTR, 4>(vtoff, vh, Nkv, (k + 1) * BC + VHR, vt1, wave & 3, k + 1 < n_tiles);
+      });
       phase_barrier();
     };
     int k = 0;
     for (; k + 1 < n_tiles; k += 2) {
-      pair(k, kbuf1, vbuf0);
-      pair(k + 1, kbuf0, vbuf1);
+      pair(k, kbuf0, kbuf1, vhd0, vhd1, vtl0, vtl1);
+      pair(k + 1, kbuf1, kbuf0, vhd1, vhd0, vtl1, vtl0);
     }
-    if (k < n_tiles) pair(k, kbuf1, vbuf0);
+    if (k < n_tiles) pair(k, kbuf0, kbuf1, vhd0, vhd1, vtl0, vtl1);
+    wait_loads();  // the last steps' loads (past the last tile: zero-size) are done
     phase_barrier();
   } else {
-    // Every step issues LPW loads per wavefront; waiting until only the newest LPW
-    // are outstanding (vmcnt counts this wavefront's loads in issue order) means
-    // the previous step's loads have landed.
-    auto wait_prev = [] { __builtin_amdgcn_s_waitcnt(0x0F70 | LPW); };  // vmcnt(LPW)
-    // Step 0: V_1 in flight.
-    load_tile<D, BC, 4>(voff, vh, Nkv, BC, vbuf1, wave & 3, n_tiles > 1);
-    wait_prev();
-    phase_barrier();
-    // Steps 2k+1 (loads K_{k+2}; softmax(k)) and 2k+2 (loads V_{k+2}; matrix(k)).
-    auto pair = [&](int k, char* kb0, char* kb1, char* vb0) {
+    phase_barrier();  // step 0: group B starts one phase behind
+    // Steps 2k+1 (softmax(k)) and 2k+2 (matrix(k)).
+    auto pair = [&](int k, char* kb1, char* vh1, char* vt0) {
       bf16x8 pb[NC][2];
-      bf16x8 va[NC][2][MT];
-      const bool live = k + 2 < n_tiles;
-      load_tile<D, BC, 4>(koff, kh, Nkv, (k + 2) * BC, kb0, wave & 3, live);
-      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, va, vb0, voffs, k >= t_full, (k + kt0) * BC, N, my_q, lane,
-                                               c, tau);
-      wait_prev();
+      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau);
       phase_barrier();
-      load_tile<D, BC, 4>(voff, vh, Nkv, (k + 2) * BC, vb0, wave & 3, live);
-      matrix_phase<D, BC>(st, s, pb, va, qreg, kb1, lane);
-      wait_prev();
+      matrix_phase<D, BC, 0>(st, s, pb, va, qreg, kb1, vt0, vh1, voffs, lane, [] {});
       phase_barrier();
     };
     int k = 0;
     for (; k + 1 < n_tiles; k += 2) {
-      pair(k, kbuf0, kbuf1, vbuf0);
-      pair(k + 1, kbuf1, kbuf0, vbuf1);
+      pair(k, kbuf1, vhd1, vtl0);
+      pair(k + 1, kbuf0, vhd0, vtl1);
     }
-    if (k < n_tiles) pair(k, kbuf0, kbuf1, vbuf0);
+    if (k < n_tiles) pair(k, kbuf1, vhd1, vtl0);
   }
 
   // Every wavefront has passed the last barrier, so no LDS tile and no Q
