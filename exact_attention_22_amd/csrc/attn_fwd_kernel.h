@@ -132,12 +132,11 @@ __device__ __forceinline__ int vswz(int r) {
 // Loads of one BC-row tile of K or V into an LDS tile buffer by NW wavefronts.
 // Each wave instruction fills 1 KiB (RPL consecutive rows); wave-load i of
 // wavefront w covers rows RPL*(NW*i + w) .. +RPL-1. With that assignment the
-// row's swizzle does not depend on i, so one per-lane byte offset (load_offset,
-// fixed for the whole kernel) serves every load of a wavefront: load i reads
-// from a buffer resource rebased by i*RPL*NW rows in scalar registers. The
-// resources end at row N, so rows past N read as zeros with no per-tile vector
-// arithmetic. (Free functions: a device member function calling these builtins
-// breaks the kernel's host-side stub.)
+// row's swizzle does not depend on i, so wave-load i reads at the per-lane byte
+// offset of load 0 plus i*STEP (load_offsets, fixed for the whole kernel). One
+// buffer resource per tile ends at row N, so rows past N read as zeros with no
+// per-load arithmetic. (Free functions: a device member function calling these
+// builtins breaks the kernel's host-side stub.)
 template <int D, int BC, int NW>
 struct LoadShape {
   static constexpr int CH = D / 8;            // 16-byte chunks per row
@@ -148,40 +147,51 @@ struct LoadShape {
 };
 
 template <int D, int BC, int NW, bool ISK>
-__device__ __forceinline__ uint32_t load_offset(int wave, int lane) {
+__device__ __forceinline__ void load_offsets(uint32_t* off, int wave, int lane) {  // off: LoadShape::LPW entries
   using S = LoadShape<D, BC, NW>;
   const int r = wave * S::RPL + lane / S::CH;  // row of load 0; load i adds RPL*NW*i rows
   const int c = (lane % S::CH) ^ (ISK ? kswz<D>(r) : vswz<D>(r));
-  return (uint32_t)(r * D + 8 * c) * 2;
+#pragma unroll
+  for (int i = 0; i < S::LPW; ++i) off[i] = (uint32_t)(r * D + 8 * c) * 2 + (uint32_t)(i * S::STEP);
 }
 
 // A tile that is not `live` (past the last tile, or starting at or past row N)
-// gets zero-size resources: its loads fill the buffer with zeros without touching
-// memory, so every step issues the same loads and the load/wait sequence has no
-// branches.
+// gets a zero-size resource: its loads fill the buffer with zeros without
+// touching memory, so every step issues the same loads and the load/wait
+// sequence has no branches.
 template <int D, int BC, int NW>
-__device__ __forceinline__ void load_tile(uint32_t off, const __bf16* head, int N, int j0, char* buf, int wave,
-                                          bool live) {
+__device__ __forceinline__ void load_tile(const uint32_t* off, const __bf16* head, int N, int j0, char* buf, int wave,
+                                          bool live) {  // off: LoadShape::LPW per-load offsets
   using S = LoadShape<D, BC, NW>;
-  live = live && j0 < N;  // a half tile can start past the last key
+  live = live && j0 < N;
   const char* base = (const char*)(head + (size_t)(live ? j0 : 0) * D);
-  const uint32_t bytes = live ? (uint32_t)(N - j0) * D * 2 : 0u;
+  // readfirstlane keeps the (uniform) record count in a scalar register: a
+  // resource in vector registers would need a loop over lanes.
+  const uint32_t rec = __builtin_amdgcn_readfirstlane(live ? (uint32_t)(N - j0) * D * 2 : 0u);
+  const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(base, rec);
 #pragma unroll
-  for (int i = 0; i < S::LPW; ++i) {
-    const uint32_t skip = (uint32_t)(i * S::STEP);
-    // readfirstlane keeps the (uniform) record count in a scalar register: the
-    // compiler computes the clamped difference on the VALU, and a resource in
-    // vector registers would need a loop over lanes.
-    const uint32_t rec = __builtin_amdgcn_readfirstlane(bytes > skip ? bytes - skip : 0u);
-    const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(base + skip, rec);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(buf + (NW * i + wave) * 1024), 16, off, 0, 0, 0);
-  }
+  for (int i = 0; i < S::LPW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(buf + (NW * i + wave) * 1024), 16, off[i], 0, 0, 0);
 }
 
 // K fragment (A operand of S^T = K Q^T): row R, 16-byte chunk c.
 template <int D>
 __device__ __forceinline__ bf16x8 k_frag(const char* kb, int R, int c) {
   return *(const bf16x8*)(kb + R * (2 * D) + ((c ^ kswz<D>(R)) << 4));
+}
+// Per-lane byte offsets of the K fragments of k-step kk for key row l32 of a
+// 32-row chunk (the chunk's 32*cc rows add a compile-time offset, which keeps
+// the swizzle since 32*cc does not change the row modulo 16); computed once per
+// kernel so that each fragment read is one instruction with an immediate offset.
+template <int D>
+__device__ __forceinline__ void k_offsets(int (&koffs)[D / 16], int lane) {
+  const int l32 = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) koffs[kk] = l32 * (2 * D) + (((2 * kk + hl) ^ kswz<D>(l32)) << 4);
+}
+template <int D>
+__device__ __forceinline__ bf16x8 k_frag_at(const char* kb, int off, int cc) {
+  return *(const bf16x8*)(kb + off + cc * 32 * (2 * D));
 }
 
 // Transpose-read addressing of the swizzled V tile. For value-feature block mt,
@@ -227,15 +237,14 @@ __device__ __forceinline__ float pair_sum(float x) {
 // cc * (D/16) + kk in [F0, F1) (chunk cc of 32 keys, k-step kk); a chunk's chain
 // starts from zero at kk = 0.
 template <int D, int NC, int F0, int F1>
-__device__ __forceinline__ void qk_part(const char* kb, const bf16x8 (&qreg)[D / 16], f32x16 (&s)[NC], int l32,
-                                        int hl) {
+__device__ __forceinline__ void qk_part(const char* kb, const bf16x8 (&qreg)[D / 16], f32x16 (&s)[NC],
+                                        const int (&koffs)[D / 16]) {
   constexpr int KK = D / 16;
 #pragma unroll
   for (int f = F0; f < F1; ++f) {
     const int cc = f / KK, kk = f % KK;
     if (kk == 0) s[cc] = f32x16{};
-    s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(kb, 32 * cc + l32, 2 * kk + hl), qreg[kk], s[cc], 0, 0,
-                                                    0);
+    s[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag_at<D>(kb, koffs[kk], cc), qreg[kk], s[cc], 0, 0, 0);
   }
 }
 
@@ -434,7 +443,8 @@ template <int D, int BC, int NLOADS, typename Loads>
 __device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 32], const bf16x8 (&pb)[BC / 32][2],
                                              bf16x8 (&va)[VSplit<D>::HKS][D / 32], const bf16x8 (&qreg)[D / 16],
                                              const char* kb, const char* vtl, const char* vhd_next,
-                                             const int (&voffs)[D / 32], int lane, Loads&& loads) {
+                                             const int (&voffs)[D / 32], const int (&koffs)[D / 16], int lane,
+                                             Loads&& loads) {
   constexpr int NC = BC / 32;
   constexpr int MT = D / 32;
   constexpr int KK = D / 16;
@@ -443,7 +453,6 @@ __device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 3
   constexpr int NQK = NC * KK;      // QK products
   constexpr int KA = MT < 4 ? MT : 4;  // K fragments read ahead of the QK products
   static_assert(NLOADS <= NQK - KA, "one tile load per late QK product");
-  const int l32 = lane & 31, hl = lane >> 5;
   // Issue priority up while this wavefront feeds the matrix core, so the
   // softmax wavefront on the same SIMD does not delay its MFMA issue.
   __builtin_amdgcn_s_setprio(1);
@@ -454,7 +463,7 @@ __device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 3
     const s16x4 hi = v_col4<D>(buf + voffs[mt], 16 * ks + 8);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto kread = [&](int f) { kf[f] = k_frag<D>(kb, 32 * (f / KK) + l32, 2 * (f % KK) + hl); };
+  auto kread = [&](int f) { kf[f] = k_frag_at<D>(kb, koffs[f % KK], f / KK); };
 #pragma unroll
   for (int g = 0; g < HKS; ++g)
 #pragma unroll
@@ -528,11 +537,14 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   const int hl = lane >> 5;
   const int N = p.N;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const uint32_t koff = load_offset<D, BC, 4, true>(wave & 3, lane);
-  const uint32_t vhoff = load_offset<D, VHR, 4, false>(wave & 3, lane);
-  const uint32_t vtoff = load_offset<D, VTR, 4, false>(wave & 3, lane);
+  uint32_t koff[LoadShape<D, BC, 4>::LPW], vhoff[LoadShape<D, VHR, 4>::LPW], vtoff[LoadShape<D, VTR, 4>::LPW];
+  load_offsets<D, BC, 4, true>(koff, wave & 3, lane);
+  load_offsets<D, VHR, 4, false>(vhoff, wave & 3, lane);
+  load_offsets<D, VTR, 4, false>(vtoff, wave & 3, lane);
   int voffs[MT];
   v_offsets<D>(voffs, lane);
+  int koffs[KK];
+  k_offsets<D>(koffs, lane);
   const float c = p.c;
   const float tau = p.tau;
 
@@ -684,7 +696,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
       const s16x4 hi = v_col4<D>(vhd0 + voffs[mt], 16 * g + 8);
       va[g][mt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
-  qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, s, l32, hl);
+  qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, s, koffs);
 
   // Every wavefront runs all n_tiles tiles of its workgroup: a tile past a causal
   // row's last visible key is fully masked (P = 0) and leaves m, l and O as they
@@ -710,7 +722,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
       softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau);
       wait_loads();
       phase_barrier();
-      matrix_phase<D, BC, NLD>(st, s, pb, va, qreg, kb1, vt0, vh1, voffs, lane, [&] {
+      matrix_phase<D, BC, NLD>(st, s, pb, va, qreg, kb1, vt0, vh1, voffs, koffs, lane, [&] {
         load_tile<D, BC, 4>(koff, kh, Nkv, (k + 2) * BC, kb0, wave & 3, k + 2 < n_tiles);
         load_tile<D, VHR, 4>(vhoff, vh, Nkv, (k + 2) * BC, vh0, wave & 3, k + 2 < n_tiles);
         load_tile<D, VTR, 4>(vtoff, vh, Nkv, (k + 1) * BC + VHR, vt1, wave & 3, k + 1 < n_tiles);
@@ -732,7 +744,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
       bf16x8 pb[NC][2];
       softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau);
       phase_barrier();
-      matrix_phase<D, BC, 0>(st, s, pb, va, qreg, kb1, vt0, vh1, voffs, lane, [] {});
+      matrix_phase<D, BC, 0>(st, s, pb, va, qreg, kb1, vt0, vh1, voffs, koffs, lane, [] {});
       phase_barrier();
     };
     int k = 0;
