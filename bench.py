@@ -27,6 +27,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# The CPU baseline's BLAS threads: every core this process may run on, unless the
+# environment already fixes the count (set before numpy or torch loads a BLAS).
+AFFINITY_CORES = len(os.sched_getaffinity(0))
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, str(AFFINITY_CORES))
+
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
@@ -327,12 +333,13 @@ def cpu_model():
 def cpu_baseline(w, target_s):
     """Time the fp64 oracle (as it stands) on a bounded sample: whole heads of the
     workload, as many as fit the target time; returned in TFLOP/s of the metric."""
-    import numpy as np
+    import numpy as np  # noqa: F401  (loads the BLAS whose threads are counted below)
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl absent: report the process's CPU share
-        cores = len(os.sched_getaffinity(0))
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [0])
+    except Exception:  # threadpoolctl absent
+        blas = 0
+    threads = blas or int(os.environ.get("OPENBLAS_NUM_THREADS") or AFFINITY_CORES)
     import oracle
     from exact_attention_22_amd import inputs
 
@@ -357,9 +364,11 @@ def cpu_baseline(w, target_s):
     heads = max(1, min(units, int(target_s / max(one, 1e-3))))
     dt = run(heads, w.seed + 1)
     flops = w.flops / units * heads
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{heads} of {units} heads of {w.name} (full rows), {dt:.1f} s fp64 numpy",
-            "seconds": round(dt, 2), "cpu_model": cpu_model(),
+            "seconds": round(dt, 2), "cpu_model": cpu_model(), "blas_threads": int(threads),
+            "host_cpus": os.cpu_count(), "affinity_cpus": AFFINITY_CORES,
+            "thread_env": {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")},
             "full_workload_seconds_extrapolated": round(dt * units / heads, 1)}
 
 

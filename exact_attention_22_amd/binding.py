@@ -169,15 +169,32 @@ def attn_fwd_varlen_check(q, k, v, o, lse, cu, B, H, Hkv, total, max_seqlen, d, 
                                        ctypes.byref(opts) if opts is not None else None)
 
 
-def _check_tensor(name, t, shape=None):
+def _check_tensor(name, t, shape=None, device=None):
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
     if t.dtype != torch.bfloat16:
         raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous [B,H,N,d]")
     if t.dim() != 4 or (shape is not None and tuple(t.shape) != shape):
         raise ValueError(f"{name} must have shape {shape or '[B,H,N,d]'}, got {tuple(t.shape)}")
+
+
+def _check_buffer(name, t, dtype, shape, device):
+    """A caller-supplied output or workspace: the C layer cannot see its size, dtype
+    or device, so all of them are checked here before its address is passed on."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
@@ -196,16 +213,18 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     B, H, N, d = shape
     _check_tensor("k", k)
     Hkv = k.shape[1]
-    _check_tensor("k", k, (B, Hkv, N, d))
-    _check_tensor("v", v, (B, Hkv, N, d))
+    _check_tensor("k", k, (B, Hkv, N, d), q.device)
+    _check_tensor("v", v, (B, Hkv, N, d), q.device)
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out_dtype must be bfloat16 or float32")
     if out is None:
         out = torch.empty(shape, dtype=out_dtype, device=q.device)
+    _check_buffer("out", out, out_dtype, shape, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_buffer("lse", lse, torch.float32, (B, H, N), q.device)
     counts = torch.empty((B, H, N), dtype=torch.int32, device=q.device) if rescale_count else None
     opts = make_opts(tau, poly_eighths, O_F32 if out_dtype == torch.float32 else O_BF16,
                      counts.data_ptr() if counts is not None else None)
@@ -238,6 +257,8 @@ def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
             raise TypeError(f"{name} must be a bfloat16 CUDA (HIP) tensor")
         if t.dim() != 3 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [heads,total,d] tensor, got {tuple(t.shape)}")
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}, got {t.device}")
     H, T, d = q.shape
     Hkv = k.shape[0]
     if tuple(k.shape) != (Hkv, T, d) or tuple(v.shape) != (Hkv, T, d):
@@ -256,8 +277,10 @@ def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
         raise TypeError("out_dtype must be bfloat16 or float32")
     if out is None:
         out = torch.empty((H, T, d), dtype=out_dtype, device=q.device)
+    _check_buffer("out", out, out_dtype, (H, T, d), q.device)
     if lse is None:
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _check_buffer("lse", lse, torch.float32, (H, T), q.device)
     counts = torch.empty((H, T), dtype=torch.int32, device=q.device) if rescale_count else None
     opts = make_opts(tau, poly_eighths, O_F32 if out_dtype == torch.float32 else O_BF16,
                      counts.data_ptr() if counts is not None else None)
@@ -292,10 +315,10 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: tor
     B, H, N, d = q.shape
     _check_tensor("k", k)
     Hkv = k.shape[1]
-    _check_tensor("k", k, (B, Hkv, N, d))
-    _check_tensor("v", v, (B, Hkv, N, d))
-    _check_tensor("o", o, (B, H, N, d))
-    _check_tensor("dout", dout, (B, H, N, d))
+    _check_tensor("k", k, (B, Hkv, N, d), q.device)
+    _check_tensor("v", v, (B, Hkv, N, d), q.device)
+    _check_tensor("o", o, (B, H, N, d), q.device)
+    _check_tensor("dout", dout, (B, H, N, d), q.device)
     if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
             or not lse.is_contiguous() or lse.device != q.device):
         raise TypeError("lse must be a contiguous float32 [B,H,N] tensor on q's device")
@@ -306,9 +329,8 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: tor
     dv = torch.empty_like(v) if dv is None else dv
     delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
     for name, t, shape in (("dq", dq, (B, H, N, d)), ("dk", dk, (B, Hkv, N, d)), ("dv", dv, (B, Hkv, N, d))):
-        _check_tensor(name, t, shape)
-    if delta.dtype != torch.float32 or tuple(delta.shape) != (B, H, N) or not delta.is_contiguous():
-        raise TypeError("delta must be a contiguous float32 [B,H,N] tensor")
+        _check_tensor(name, t, shape, q.device)
+    _check_buffer("delta", delta, torch.float32, (B, H, N), q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, Hkv, N, d, causal, scale,
@@ -334,19 +356,24 @@ def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
     B, H, N, d = q.shape
     _check_tensor("k", k)
     Hkv = k.shape[1]
-    _check_tensor("k", k, (B, Hkv, N, d))
-    _check_tensor("v", v, (B, Hkv, N, d))
+    _check_tensor("k", k, (B, Hkv, N, d), q.device)
+    _check_tensor("v", v, (B, Hkv, N, d), q.device)
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out_dtype must be bfloat16 or float32")
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    _check_buffer("out", out, out_dtype, (B, H, N, d), q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_buffer("lse", lse, torch.float32, (B, H, N), q.device)
     need = splitkv_workspace_size(B, H, N, d, n_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_buffer("workspace", workspace, torch.uint8, None, q.device)
+    if workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
     opts = make_opts(tau, 0, O_F32 if out_dtype == torch.float32 else O_BF16, None)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = lib().attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
@@ -403,10 +430,8 @@ def attention_fp8(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, scales, ca
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
     out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, N, d) or not out.is_contiguous():
-        raise TypeError("out must be a contiguous bfloat16 [B,H,N,d] tensor")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise TypeError("lse must be a contiguous float32 [B,H,N] tensor")
+    _check_buffer("out", out, torch.bfloat16, (B, H, N, d), q.device)
+    _check_buffer("lse", lse, torch.float32, (B, H, N), q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = attn_fwd_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
                       causal, scale, qs, ks, vs, tau, stream)
@@ -441,6 +466,8 @@ def attention_backward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() \
                 or t.dim() != 3:
             raise TypeError(f"{name} must be a contiguous bfloat16 3-d CUDA tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}, got {t.device}")
     H, T, d = q.shape
     Hkv = k.shape[0]
     if tuple(k.shape) != (Hkv, T, d) or tuple(v.shape) != (Hkv, T, d):

@@ -238,6 +238,36 @@ def test_writes_only_its_outputs():
     assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, what="guarded")
 
 
+def test_python_wrapper_rejects_bad_outputs():
+    """Caller-supplied out and lse are checked before the C call, which cannot see
+    their size, dtype or device."""
+    dev = device()
+    q = torch.zeros((2, 3, 40, 64), dtype=torch.bfloat16, device=dev)
+    bad_out = [
+        (torch.empty(q.shape, dtype=torch.float32, device=dev), TypeError),        # fp32 O for bf16 out_dtype
+        (torch.empty((2, 3, 39, 64), dtype=torch.bfloat16, device=dev), ValueError),  # undersized
+        (torch.empty((2, 40, 3, 64), dtype=torch.bfloat16, device=dev).transpose(1, 2), ValueError),  # strided
+        (torch.empty(q.shape, dtype=torch.bfloat16), ValueError),                  # host memory
+    ]
+    for out, exc in bad_out:
+        with pytest.raises(exc):
+            binding.attention(q, q, q, out=out)
+    for lse, exc in [(torch.empty((2, 3, 40), dtype=torch.float64, device=dev), TypeError),
+                     (torch.empty((2, 3, 20), dtype=torch.float32, device=dev), ValueError),
+                     (torch.empty((2, 3, 40), dtype=torch.float32), ValueError)]:
+        with pytest.raises(exc):
+            binding.attention(q, q, q, lse=lse)
+    with pytest.raises(TypeError):
+        binding.attention(q, q, q, out_dtype=torch.float32, out=torch.empty(q.shape, dtype=torch.bfloat16, device=dev))
+    # packed batches: [H, total, d] outputs
+    qv = torch.zeros((3, 100, 64), dtype=torch.bfloat16, device=dev)
+    cu = torch.tensor([0, 60, 100], dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        binding.attention_varlen(qv, qv, qv, cu, out=torch.empty((3, 99, 64), dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        binding.attention_varlen(qv, qv, qv, cu, lse=torch.empty((3, 100), dtype=torch.float32))
+
+
 def test_python_wrapper_rejects_bad_tensors():
     dev = device()
     q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device=dev)

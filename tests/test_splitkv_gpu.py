@@ -82,4 +82,15 @@ def test_splitkv_rejects_bad_workspace():
     with pytest.raises(binding.AttnError):
         binding.attention_splitkv(q, q, q, n_splits=2, workspace=small)
     with pytest.raises(binding.AttnError):
-        binding.attention_splitkv(q, q, q, n_splits=2, workspace=q.view(torch.uint8))  # overlaps q
+        binding.attention_splitkv(q, q, q, n_splits=2, workspace=q.view(torch.uint8).flatten())  # overlaps q
+    # caught by the binding before the C call: wrong dtype, wrong device, not 1-D, fp32 out for bf16
+    with pytest.raises(TypeError):
+        binding.attention_splitkv(q, q, q, n_splits=2, workspace=torch.empty(need // 4, dtype=torch.float32,
+                                                                             device=dev))
+    with pytest.raises(ValueError):
+        binding.attention_splitkv(q, q, q, n_splits=2, workspace=torch.empty(need, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        binding.attention_splitkv(q, q, q, n_splits=2, workspace=torch.empty((2, need), dtype=torch.uint8,
+                                                                             device=dev))
+    with pytest.raises(TypeError):
+        binding.attention_splitkv(q, q, q, n_splits=2, out=torch.empty(q.shape, dtype=torch.float32, device=dev))
