@@ -25,8 +25,10 @@ EXPORTS = ["attn_fwd", "attn_fwd_ex", "attn_fwd_check", "attn_fwd_opts_init", "a
            "attn_last_error", "attn_abi_version", "attn_exp2_poly_host", "attn_fwd_tile_shape",
            "attn_fwd_gqa", "attn_fwd_gqa_check", "attn_fwd_varlen", "attn_fwd_varlen_check",
            "attn_bwd", "attn_bwd_check", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size",
-           "attn_fwd_fp8", "attn_fwd_fp8_check", "attn_bwd_varlen", "attn_bwd_varlen_check"]
-ABI_VERSION = 7
+           "attn_fwd_fp8", "attn_fwd_fp8_check", "attn_bwd_varlen", "attn_bwd_varlen_check",
+           "attn_fwd_splitkv_noalloc"]
+ABI_VERSION = 8
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
 
 
 class AttnFwdOpts(ctypes.Structure):
@@ -72,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t,
                                        ctypes.POINTER(AttnFwdOpts), vp]
         L.attn_fwd_splitkv.restype = i
+        L.attn_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i,
+                                               ctypes.POINTER(AttnFwdOpts), vp]
+        L.attn_fwd_splitkv_noalloc.restype = i
         L.attn_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
         L.attn_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
         bwd_args = [vp] * 10 + [i, i, i, i, i, i, f]
@@ -379,6 +384,34 @@ def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
     st = lib().attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
                                 Hkv, N, d, int(causal), scale, n_splits, workspace.data_ptr(),
                                 workspace.numel() * workspace.element_size(), ctypes.byref(opts), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, last_error())
+    return out, lse
+
+
+def attention_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                              lse: torch.Tensor, causal: bool = False, scale: float | None = None,
+                              n_splits: int = 0, *, tau: float = 8.0):
+    """attention_splitkv without a workspace: the partial results go to the library's
+    device scratch array (NOALLOC_SCRATCH_BYTES per GPU). The caller passes the
+    outputs (out: bfloat16 or float32 [B,H,N,d], lse: float32 [B,H,N]); nothing is
+    allocated here either. Calls that overlap on one GPU race. Returns (out, lse)."""
+    _check_tensor("q", q)
+    B, H, N, d = q.shape
+    _check_tensor("k", k)
+    Hkv = k.shape[1]
+    _check_tensor("k", k, (B, Hkv, N, d), q.device)
+    _check_tensor("v", v, (B, Hkv, N, d), q.device)
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be a bfloat16 or float32 tensor")
+    _check_buffer("out", out, out.dtype, (B, H, N, d), q.device)
+    _check_buffer("lse", lse, torch.float32, (B, H, N), q.device)
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+    opts = make_opts(tau, 0, O_F32 if out.dtype == torch.float32 else O_BF16, None)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib().attn_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                        B, H, Hkv, N, d, int(causal), scale, n_splits, ctypes.byref(opts), stream)
     if st != ATTN_OK:
         raise AttnError(st, last_error())
     return out, lse

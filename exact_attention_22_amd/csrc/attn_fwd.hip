@@ -9,6 +9,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -352,6 +353,35 @@ Problem packed(const void* q, const void* k, const void* v, const void* o, const
   return Problem{q, k, v, const_cast<void*>(o), const_cast<float*>(lse), cu, true, B, H, Hkv, total, max_seqlen, d, scale};
 }
 
+// Scratch of attn_fwd_splitkv_noalloc: a file-scope device array that every GPU
+// the library runs on holds until the process ends. In host code its name is a
+// host-side stand-in, not a device address; host code only ever uses the address
+// hipGetSymbolAddress returns on the device that is current, kept per device.
+static __device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+// Device address of this device's scratch array (nullptr and a message on error),
+// looked up once per device on its first use.
+void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    fail(ATTN_ERR_HIP, "no current device for the scratch array");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(ATTN_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -411,6 +441,21 @@ size_t attn_fwd_splitkv_workspace_size(int B, int H, int N, int d, int n_splits)
   return split_workspace_bytes(B, H, N, d, splits);
 }
 
+attn_status_t attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                       int H, int Hkv, int N, int d, int causal, float scale, int n_splits,
+                                       const attn_fwd_opts* opts, void* stream) {
+  const Problem P = dense(q, k, v, o, lse, B, H, Hkv, N, d, scale);
+  // sizes the check in run_split rejects get no scratch lookup either
+  const size_t need = attn_fwd_splitkv_workspace_size(B, H, N, d, n_splits);
+  if (need > ATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(ATTN_ERR_DIM, "split-key partials need %zu bytes; the library's scratch holds %zu", need,
+                (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
+  // need == 0 only for invalid or empty sizes: run_split then reports the
+  // argument error (or does nothing) before it would look at the workspace
+  void* ws = need ? scratch_address() : nullptr;
+  if (need && !ws) return ATTN_ERR_HIP;
+  return run_split(P, causal, n_splits, ws, ATTN_NOALLOC_SCRATCH_BYTES, opts, stream);
+}
 attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                int Hkv, int N, int d, int causal, float scale, int n_splits, void* workspace,
                                size_t workspace_bytes, const attn_fwd_opts* opts, void* stream) {

@@ -49,8 +49,9 @@ extern "C" {
  * 4: adds attn_bwd and attn_bwd_check (backward pass, declared in attn_bwd.h).
  * 5: adds attn_fwd_splitkv and attn_fwd_splitkv_workspace_size (split keys).
  * 6: adds attn_fwd_fp8 and attn_fwd_fp8_check (FP8 e4m3 inputs, declared in attn_fp8.h).
- * 7: adds attn_bwd_varlen and attn_bwd_varlen_check (declared in attn_bwd.h). */
-#define ATTN_ABI_VERSION 7
+ * 7: adds attn_bwd_varlen and attn_bwd_varlen_check (declared in attn_bwd.h).
+ * 8: adds attn_fwd_splitkv_noalloc. */
+#define ATTN_ABI_VERSION 8
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -235,6 +236,30 @@ attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void
 /* Workspace bytes attn_fwd_splitkv needs for these sizes (0 for invalid or
  * empty sizes). Host only. */
 size_t attn_fwd_splitkv_workspace_size(int B, int H, int N, int d, int n_splits);
+
+/* Size of the device scratch array attn_fwd_splitkv_noalloc uses (64 MiB). */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * attn_fwd_splitkv_noalloc - attn_fwd_splitkv for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. The split-key partial results go to
+ * a scratch array of ATTN_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * every GPU it runs on, for the life of the process (its address is looked up
+ * once per device, on the first call there). The call allocates nothing and
+ * frees nothing; the caller still passes q, k, v, o and lse.
+ *   Sizes whose workspace (attn_fwd_splitkv_workspace_size) exceeds the scratch
+ *   array return ATTN_ERR_DIM with the sizes in attn_last_error(); nothing is
+ *   launched. The scratch contents on entry do not matter (every partial result
+ *   the merge reads is written by the same call).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ *   (other streams, other host threads) race and give undefined results.
+ * Arguments, results and other errors as for attn_fwd_splitkv; ATTN_ERR_HIP if
+ * the scratch address cannot be obtained.
+ */
+attn_status_t attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                       int B, int H, int Hkv, int N, int d, int causal, float scale,
+                                       int n_splits, const attn_fwd_opts* opts, void* stream);
 
 /* Tile shape the kernel uses for head dim d: query rows per workgroup and keys
  * per KV tile (the granularity of the online softmax and of the rescale

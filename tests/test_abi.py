@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(bnd.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.attn_abi_version() == bnd.ABI_VERSION == 7
+    assert lib.attn_abi_version() == bnd.ABI_VERSION == 8
 
 
 def check(*args, **kw):
