@@ -33,6 +33,11 @@ attn_status_t validate(const void* q, const void* k, const void* vt, const void*
   const int64_t tiles = (int64_t)B * H * ((N + attn_fp8::kMinRows - 1) / attn_fp8::kMinRows);
   if (rows > (int64_t)1 << 40 || tiles > INT32_MAX / 2 || ldv > INT32_MAX)
     return fail(ATTN_ERR_DIM, "problem too large: B*H*N=%lld", (long long)rows);
+  // within one head the kernel forms byte offsets such as (N - j0) * d and
+  // d * ldv - j0 in 32 bits, and its buffer resources count bytes in 32 bits
+  if ((ldv + 64) * d > INT32_MAX)
+    return fail(ATTN_ERR_DIM, "N=%d too large: one head's %lld x %d bytes exceed 32-bit offsets", N,
+                (long long)ldv, d);
   if (!q || !k || !vt || !o || !lse) return fail(ATTN_ERR_NULL, "NULL tensor pointer");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)vt | (uintptr_t)o) & 15)
     return fail(ATTN_ERR_MISALIGNED, "q, k, vt and o must be 16-byte aligned");

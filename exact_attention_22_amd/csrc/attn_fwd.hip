@@ -234,8 +234,9 @@ attn_status_t run(const Problem& P, int causal, const attn_fwd_opts* opts, void*
   p.per_xcd = (p.total_tiles + 7) / 8;
   // c = scale * log2(e) in fp32. Masked scores are set to -inf (+inf for a negative
   // scale) and rely on s*c - m = -inf; for scale == 0 that product would be NaN, so
-  // 0 is replaced by 2^-100: |s| <= 2^17 for bf16 inputs with d <= 128, hence
-  // |s*c| < 2^-82 and 2^(s*c - m) rounds to exactly 1.0f, as with c = 0.
+  // 0 is replaced by 2^-100. For inputs with |q|, |k| < 2^33 (at d <= 128,
+  // |s| < 2^73), every x = s*c - m then has |x| < 2^-26 and 2^x rounds to exactly
+  // 1.0f, as with c = 0 (uniform weights over the visible keys).
   p.c = P.scale * 1.44269504088896341f;
   if (p.c == 0.f) p.c = 0x1p-100f;
   p.tau = o2.rescale_tau_log2;

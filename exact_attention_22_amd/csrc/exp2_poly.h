@@ -14,8 +14,9 @@
 // the relative error of p(f) / 2^f on [0, 1], produced by gen_exp2_poly.py in
 // this directory: max relative error 1.03e-4, below the bfloat16 half-ulp
 // (2^-9) that the probabilities are rounded to afterwards. p(0) = 1 makes
-// 2^0 = 1 exactly, as with the hardware instruction. Inputs below -127 are
-// clamped to -127 (the result, 2^-127, is far below any rounding of the sum).
+// 2^0 = 1 exactly, as with the hardware instruction. Inputs below -150 are
+// clamped to -150, where 2^n underflows to exactly 0: a masked key (x = -inf)
+// gets P = 0, as with the hardware instruction.
 #ifndef ATTN_EXP2_POLY_H
 #define ATTN_EXP2_POLY_H
 
@@ -32,7 +33,7 @@
 #endif
 
 ATTN_HD inline float attn_exp2_poly(float x) {
-  x = fmaxf(x, -127.0f);
+  x = fmaxf(x, -150.0f);
   const float n = floorf(x);
   const float f = x - n;
   const float p = fmaf(fmaf(fmaf(ATTN_EXP2_C3, f, ATTN_EXP2_C2), f, ATTN_EXP2_C1), f, 1.0f);

@@ -133,11 +133,11 @@ def test_exp2_polynomial_error_bound():
     ys = np.empty_like(fs)
     lib.attn_exp2_poly_host(fs.ctypes.data, ys.ctypes.data, fs.size)
     assert np.all(np.diff(ys) >= 0)
-    # clamped far below: tiny, non-negative, no NaN
-    lo = np.array([-1e30, -200.0, -np.inf], dtype=np.float32)
+    # far below (masked keys are -inf): exactly 0, as with the hardware instruction
+    lo = np.array([-1e30, -200.0, -151.0, -np.inf], dtype=np.float32)
     ylo = np.empty_like(lo)
     lib.attn_exp2_poly_host(lo.ctypes.data, ylo.ctypes.data, lo.size)
-    assert np.all(ylo >= 0) and np.all(ylo < 1e-37)
+    assert np.all(ylo == 0.0), ylo
 
 
 def gqa_check(*args, **kw):
@@ -283,6 +283,7 @@ def test_fp8_valid_and_empty():
 @pytest.mark.parametrize("patch,code", [
     (dict(q=None), 1), (dict(lse=None), 1),
     (dict(B=-1), 2), (dict(N=-3), 2), (dict(B=1 << 20, H=1 << 10, N=1 << 20), 2),
+    (dict(B=1, H=1, N=(1 << 24) - 64), 2), (dict(B=1, H=1, N=1 << 25, d=64), 2),  # 32-bit offsets in one head
     (dict(d=96), 3), (dict(tau=8.5), 3), (dict(tau=-1.0), 3), (dict(tau=float("nan")), 3),
     (dict(q=Q + 8), 4), (dict(vt=V + 4), 4), (dict(lse=L + 2), 4),
     (dict(scale=0.0), 5), (dict(scale=-1.0), 5), (dict(q_scale=float("inf")), 5), (dict(v_scale=0.0), 5),
