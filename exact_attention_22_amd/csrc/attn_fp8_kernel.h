@@ -1,10 +1,9 @@
 // attn_fp8_kernel.h - FP8 (e4m3) exact-attention forward kernel for gfx950.
 //
 // The FP8 form of the method: both products run on 8-bit floating-point
-// operands (page "FlashAttention 4: faster, more memory-efficient attention for
-// LLMs", section "What's new in FlashAttention 4", on the low-precision path;
-// page "We reverse-engineered Flash Attention 4", on the FP8 path of the
-// earlier Hopper kernel). Everything else is the tiled online softmax of the
+// operands (page "Flash Attention" glossary, section "FlashAttention-3 and the
+// FP8 era", and its hardware section on FP8 and lower-precision formats).
+// Everything else is the tiled online softmax of the
 // bf16 kernel (page "Flash Attention" glossary, sections "Tiling with SRAM" and
 // "Online softmax and recomputation"), with the adaptive rescale of page
 // "FlashAttention 4: ...", section "Smarter online softmax rescaling (new in FA4)".

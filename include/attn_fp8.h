@@ -2,10 +2,10 @@
  * attn_fp8.h - C ABI of the MI355X (gfx950) FP8 exact-attention forward pass.
  *
  * Operation: the exact attention of attn_fwd.h evaluated on 8-bit floating-point
- * inputs, with both products on the FP8 matrix cores (page "FlashAttention 4:
- * faster, more memory-efficient attention for LLMs", section "What's new in
- * FlashAttention 4", on the low-precision path; page "We reverse-engineered
- * Flash Attention 4", on the FP8 path of the earlier Hopper kernel).
+ * inputs, with both products on the FP8 matrix cores (page "Flash Attention"
+ * glossary, section "FlashAttention-3 and the FP8 era": FP8 inputs halve the
+ * memory traffic again while keeping the accuracy; its hardware section on the
+ * H100's FP8 and the B200's low-precision formats).
  *
  * Inputs are OCP e4m3 ("e4m3fn") codes: sign, 4 exponent bits (bias 7), 3
  * mantissa bits, subnormals, S.1111.111 = NaN, no infinities, largest finite

@@ -205,9 +205,11 @@ attn_status_t attn_fwd_varlen_check(const void* q, const void* k, const void* v,
 /*
  * attn_fwd_splitkv - attn_fwd_gqa with the keys of every query tile split into
  * n_splits ranges computed by separate workgroups, for shapes with too few
- * query tiles to occupy the GPU and for very long sequences (page "FlashAttention
- * 4: faster, more memory-efficient attention for LLMs", section "Why attention
- * kernels still dominate LLM cost", on long contexts). Unit s of a query tile
+ * query tiles to occupy the GPU and for very long sequences (page "Flash
+ * Attention" glossary, overview section and its list of benefits, on contexts of
+ * 128k and 1M tokens; page "FlashAttention 4: faster, more memory-efficient
+ * attention for LLMs", section "Conclusion", on forward throughput at long
+ * sequence lengths). Unit s of a query tile
  * computes O_s and LSE_s over its key range into the workspace (fp32); a second
  * kernel merges them per row: LSE = log sum_s exp(LSE_s), O = sum_s
  * exp(LSE_s - LSE) O_s. The result equals attn_fwd_gqa's up to rounding.

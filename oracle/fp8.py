@@ -3,10 +3,10 @@
 Only tests, the smoke check and the benchmark's CPU-baseline leg may import this
 module. It shares no code with the HIP path and never imports it.
 
-The FP8 variant of the method ([LK] "FlashAttention 4: faster, more
-memory-efficient attention for LLMs", section "What's new in FlashAttention 4",
-and [EN] "We reverse-engineered Flash Attention 4", on the FP8 path of the
-earlier Hopper kernel) runs the two products on 8-bit floating-point inputs.
+The FP8 variant of the method (page "Flash Attention" glossary, section
+"FlashAttention-3 and the FP8 era", and its hardware section on the H100's FP8
+and the B200's low-precision formats) runs the two products on 8-bit
+floating-point inputs.
 The pages give neither the format nor the scaling; the readings used here:
 
   * inputs are OCP e4m3 ("e4m3fn") codes: 1 sign bit, 4 exponent bits with
