@@ -37,7 +37,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "exact_attention_22_amd", "csrc")
-KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip", "exp2_poly.h")
+KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip", "attn_fwd_launch.h", "attn_fwd_launch_impl.h",
+                  "attn_fwd_d128_full.hip", "exp2_poly.h")
 
 # HBM bytes per launch of the headline kernel from two rocprofv3 --pmc runs
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch), each scaled by what the same

@@ -26,15 +26,16 @@ EXPORTS = ["attn_fwd", "attn_fwd_ex", "attn_fwd_check", "attn_fwd_opts_init", "a
            "attn_fwd_gqa", "attn_fwd_gqa_check", "attn_fwd_varlen", "attn_fwd_varlen_check",
            "attn_bwd", "attn_bwd_check", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size",
            "attn_fwd_fp8", "attn_fwd_fp8_check", "attn_bwd_varlen", "attn_bwd_varlen_check",
-           "attn_fwd_splitkv_noalloc"]
-ABI_VERSION = 8
+           "attn_fwd_splitkv_noalloc", "attn_fwd_fp8_ex"]
+ABI_VERSION = 9
+SCHEDULE_PIPELINED, SCHEDULE_REFERENCE = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
 
 
 class AttnFwdOpts(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_size_t), ("rescale_tau_log2", ctypes.c_float),
                 ("exp2_poly_eighths", ctypes.c_int), ("o_dtype", ctypes.c_int),
-                ("rescale_count", ctypes.c_void_p)]
+                ("rescale_count", ctypes.c_void_p), ("schedule", ctypes.c_int)]
 
 
 class AttnError(RuntimeError):
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
         fp8_args = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, f, f, f]
         L.attn_fwd_fp8.argtypes = fp8_args + [vp]
         L.attn_fwd_fp8.restype = i
+        L.attn_fwd_fp8_ex.argtypes = fp8_args + [i, vp]
+        L.attn_fwd_fp8_ex.restype = i
         L.attn_fwd_fp8_check.argtypes = fp8_args
         L.attn_fwd_fp8_check.restype = i
         L.attn_fwd_opts_init.argtypes = [ctypes.POINTER(AttnFwdOpts)]
@@ -110,13 +113,15 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def make_opts(tau: float = 8.0, poly_eighths: int = 0, o_dtype: int = O_BF16, rescale_count: int | None = None):
+def make_opts(tau: float = 8.0, poly_eighths: int = 0, o_dtype: int = O_BF16, rescale_count: int | None = None,
+              schedule: int = SCHEDULE_PIPELINED):
     opts = AttnFwdOpts()
     lib().attn_fwd_opts_init(ctypes.byref(opts))
     opts.rescale_tau_log2 = tau
     opts.exp2_poly_eighths = poly_eighths
     opts.o_dtype = o_dtype
     opts.rescale_count = rescale_count
+    opts.schedule = schedule
     return opts
 
 
@@ -205,13 +210,14 @@ def _check_buffer(name, t, dtype, shape, device):
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
               scale: float | None = None, *, tau: float = 8.0, poly_eighths: int = 0,
               out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
-              lse: torch.Tensor | None = None, rescale_count: bool = False):
+              lse: torch.Tensor | None = None, rescale_count: bool = False, schedule: int = SCHEDULE_PIPELINED):
     """Exact attention forward on the current stream: returns (O, LSE[, rescale counts]).
 
     q: bfloat16 [B,H,N,d]; k, v: bfloat16 [B,Hkv,N,d] with Hkv dividing H (Hkv < H is
     grouped-query attention: query head h reads key/value head h // (H // Hkv)); all
     contiguous device tensors. scale defaults to 1/sqrt(d) (as a float32). O has
-    `out_dtype` (bfloat16 or float32); LSE is float32 [B,H,N].
+    `out_dtype` (bfloat16 or float32); LSE is float32 [B,H,N]. schedule =
+    SCHEDULE_REFERENCE runs the race-check schedule (bitwise the same results).
     """
     _check_tensor("q", q)
     shape = tuple(q.shape)
@@ -232,7 +238,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     _check_buffer("lse", lse, torch.float32, (B, H, N), q.device)
     counts = torch.empty((B, H, N), dtype=torch.int32, device=q.device) if rescale_count else None
     opts = make_opts(tau, poly_eighths, O_F32 if out_dtype == torch.float32 else O_BF16,
-                     counts.data_ptr() if counts is not None else None)
+                     counts.data_ptr() if counts is not None else None, schedule)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     if Hkv == H:
         st = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -249,7 +255,7 @@ def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
                      max_seqlen: int | None = None, causal: bool = False, scale: float | None = None, *,
                      tau: float = 8.0, poly_eighths: int = 0, out_dtype: torch.dtype = torch.bfloat16,
                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                     rescale_count: bool = False):
+                     rescale_count: bool = False, schedule: int = SCHEDULE_PIPELINED):
     """Attention over packed variable-length sequences on the current stream.
 
     q: bfloat16 [H,total,d]; k, v: bfloat16 [Hkv,total,d]; cu_seqlens: int32 [B+1]
@@ -288,7 +294,7 @@ def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
     _check_buffer("lse", lse, torch.float32, (H, T), q.device)
     counts = torch.empty((H, T), dtype=torch.int32, device=q.device) if rescale_count else None
     opts = make_opts(tau, poly_eighths, O_F32 if out_dtype == torch.float32 else O_BF16,
-                     counts.data_ptr() if counts is not None else None)
+                     counts.data_ptr() if counts is not None else None, schedule)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                          cu_seqlens.data_ptr(), B, H, Hkv, T, max_seqlen, d, causal, scale, opts, stream)
@@ -352,7 +358,8 @@ def splitkv_workspace_size(B: int, H: int, N: int, d: int, n_splits: int = 0) ->
 def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                       scale: float | None = None, n_splits: int = 0, *, tau: float = 8.0,
                       out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
-                      lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+                      lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      schedule: int = SCHEDULE_PIPELINED):
     """Exact attention with split keys (n_splits units per query tile, 0 = automatic),
     merged by log-sum-exp weights. Same shapes and results (up to rounding) as
     `attention`. `workspace`: a uint8 device tensor of at least
@@ -379,7 +386,7 @@ def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
     _check_buffer("workspace", workspace, torch.uint8, None, q.device)
     if workspace.dim() != 1:
         raise ValueError("workspace must be a 1-D uint8 tensor")
-    opts = make_opts(tau, 0, O_F32 if out_dtype == torch.float32 else O_BF16, None)
+    opts = make_opts(tau, 0, O_F32 if out_dtype == torch.float32 else O_BF16, None, schedule)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = lib().attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
                                 Hkv, N, d, int(causal), scale, n_splits, workspace.data_ptr(),
@@ -423,6 +430,13 @@ def attn_fwd_fp8(q, k, vt, o, lse, B, H, N, d, causal, scale, q_scale, k_scale, 
                               stream)
 
 
+def attn_fwd_fp8_ex(q, k, vt, o, lse, B, H, N, d, causal, scale, q_scale, k_scale, v_scale, tau, schedule,
+                    stream) -> int:
+    """The C entry point with a kernel schedule; returns the status code."""
+    return lib().attn_fwd_fp8_ex(q, k, vt, o, lse, B, H, N, d, int(causal), scale, q_scale, k_scale, v_scale, tau,
+                                 schedule, stream)
+
+
 def attn_fwd_fp8_check(q, k, vt, o, lse, B, H, N, d, causal, scale, q_scale, k_scale, v_scale, tau) -> int:
     return lib().attn_fwd_fp8_check(q, k, vt, o, lse, B, H, N, d, int(causal), scale, q_scale, k_scale, v_scale,
                                     tau)
@@ -435,7 +449,7 @@ def fp8_ldv(N: int) -> int:
 
 def attention_fp8(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, scales, causal: bool = False,
                   scale: float | None = None, *, tau: float = 8.0, out: torch.Tensor | None = None,
-                  lse: torch.Tensor | None = None):
+                  lse: torch.Tensor | None = None, schedule: int = SCHEDULE_PIPELINED):
     """FP8 exact attention forward on the current stream: returns (O bf16 [B,H,N,d], LSE fp32 [B,H,N]).
 
     q, k: e4m3 codes [B,H,N,d] (uint8 or torch.float8_e4m3fn); vt: V transposed, e4m3 codes
@@ -466,8 +480,8 @@ def attention_fp8(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, scales, ca
     _check_buffer("out", out, torch.bfloat16, (B, H, N, d), q.device)
     _check_buffer("lse", lse, torch.float32, (B, H, N), q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = attn_fwd_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
-                      causal, scale, qs, ks, vs, tau, stream)
+    st = attn_fwd_fp8_ex(q.data_ptr(), k.data_ptr(), vt.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                         causal, scale, qs, ks, vs, tau, schedule, stream)
     if st != ATTN_OK:
         raise AttnError(st, last_error())
     return out, lse

@@ -29,13 +29,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-SOURCES = ("attn_fwd.hip", "attn_bwd.hip", "attn_fp8.hip")
+# attn_fwd.hip holds the host code of the forward entry points; the forward kernel's
+# variants are instantiated per head dim and mask in their own units so that they
+# compile in parallel.
+SOURCES = ("attn_fwd.hip", "attn_fwd_d128_full.hip", "attn_fwd_d128_causal.hip", "attn_fwd_d64_full.hip",
+           "attn_fwd_d64_causal.hip", "attn_bwd.hip", "attn_fp8.hip")
 
 
-def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
+def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False,
+          link_extra: list[str] | None = None, log: list | None = None) -> str:
     """Always recompiles; returns the path of the shared library.
 
-    Each translation unit is compiled to an object in parallel, then linked."""
+    Each translation unit is compiled to an object in parallel, then linked.
+    `extra` is added to every compile line, `link_extra` to the link line; with
+    `log`, each unit's compiler output is appended to it as (source, text)."""
     tmp = out + ".tmp"
     objs = [f"{out}.{os.path.splitext(src)[0]}.o" for src in SOURCES]
     base = [hipcc(), f"--offload-arch={ARCH}", *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC]
@@ -46,14 +53,16 @@ def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False)
             print(" ".join(cmd), flush=True)
         procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
     failed = False
-    for p in procs:
+    for src, p in zip(SOURCES, procs):
         text, _ = p.communicate()
+        if log is not None:
+            log.append((src, text))
         if p.returncode != 0:
             sys.stderr.write(text)
             failed = True
     if failed:
         raise RuntimeError("hipcc failed")
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp, *(link_extra or [])]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

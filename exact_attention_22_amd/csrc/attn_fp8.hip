@@ -54,10 +54,11 @@ attn_status_t validate(const void* q, const void* k, const void* vt, const void*
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch(const attn_fp8::Fp8Params& p, hipStream_t stream) {
+hipError_t launch(const attn_fp8::Fp8Params& p, bool ref, hipStream_t stream) {
   void* args[] = {const_cast<attn_fp8::Fp8Params*>(&p)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fp8::attn_fwd_fp8_kernel<D, CAUSAL>),
-                         dim3(8 * p.per_xcd), dim3(64 * attn_fp8::Shape<D>::NW), args, 0, stream);
+  const void* fn = ref ? reinterpret_cast<const void*>(&attn_fp8::attn_fwd_fp8_kernel<D, CAUSAL, true>)
+                       : reinterpret_cast<const void*>(&attn_fp8::attn_fwd_fp8_kernel<D, CAUSAL, false>);
+  return hipLaunchKernel(fn, dim3(8 * p.per_xcd), dim3(64 * attn_fp8::Shape<D>::NW), args, 0, stream);
 }
 
 }  // namespace
@@ -72,12 +73,15 @@ attn_status_t attn_fwd_fp8_check(const void* q, const void* k, const void* vt, c
   return validate(q, k, vt, o, lse, B, H, N, d, scale, q_scale, k_scale, v_scale, tau, &work);
 }
 
-attn_status_t attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, int B, int H, int N,
-                           int d, int causal, float scale, float q_scale, float k_scale, float v_scale, float tau,
-                           void* stream) {
+attn_status_t attn_fwd_fp8_ex(const void* q, const void* k, const void* vt, void* o, float* lse, int B, int H,
+                              int N, int d, int causal, float scale, float q_scale, float k_scale, float v_scale,
+                              float tau, int schedule, void* stream) {
   bool work = false;
-  const attn_status_t st = validate(q, k, vt, o, lse, B, H, N, d, scale, q_scale, k_scale, v_scale, tau, &work);
+  attn_status_t st = validate(q, k, vt, o, lse, B, H, N, d, scale, q_scale, k_scale, v_scale, tau, &work);
+  if (st == ATTN_OK && schedule != ATTN_SCHEDULE_PIPELINED && schedule != ATTN_SCHEDULE_REFERENCE)
+    st = fail(ATTN_ERR_OPTS, "schedule %d", schedule);
   if (st != ATTN_OK || !work) return st;
+  const bool ref = schedule == ATTN_SCHEDULE_REFERENCE;
   attn_fp8::Fp8Params p;
   p.q = (const uint8_t*)q;
   p.k = (const uint8_t*)k;
@@ -96,11 +100,18 @@ attn_status_t attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (d == 128)
-    e = causal ? launch<128, true>(p, s) : launch<128, false>(p, s);
+    e = causal ? launch<128, true>(p, ref, s) : launch<128, false>(p, ref, s);
   else
-    e = causal ? launch<64, true>(p, s) : launch<64, false>(p, s);
+    e = causal ? launch<64, true>(p, ref, s) : launch<64, false>(p, ref, s);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ATTN_OK;
+}
+
+attn_status_t attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, int B, int H, int N,
+                           int d, int causal, float scale, float q_scale, float k_scale, float v_scale, float tau,
+                           void* stream) {
+  return attn_fwd_fp8_ex(q, k, vt, o, lse, B, H, N, d, causal, scale, q_scale, k_scale, v_scale, tau,
+                         ATTN_SCHEDULE_PIPELINED, stream);
 }
 
 }  // extern "C"

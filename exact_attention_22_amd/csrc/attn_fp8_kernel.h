@@ -44,6 +44,12 @@
 // registers into double-buffered LDS, one barrier per tile: the global loads of
 // tile t+1 are issued before tile t's products and written to the other buffer
 // after them. Two workgroups share a compute unit.
+//
+// REF = true instantiates a reference schedule for race checks: each tile is
+// loaded and stored to LDS between two block-wide barriers and only then read,
+// with one buffer and no load in flight during the products. The arithmetic is
+// the same instructions in the same order, so its results are bitwise equal to
+// the pipelined schedule's.
 #ifndef ATTN_FP8_KERNEL_H
 #define ATTN_FP8_KERNEL_H
 
@@ -194,7 +200,7 @@ __device__ __forceinline__ i32x8 read32(const char* base, int r, int ch, int swz
   return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool REF = false>
 __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_fp8_kernel(const Fp8Params p) {
   constexpr int kRows = Shape<D>::ROWS;
   constexpr int MQ = D / 64;  // QK products per 32-key block
@@ -263,15 +269,9 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
   stage_store<D>(stg, kbuf[0], vbuf[0], tid);
   __syncthreads();
 
-  // One tile step; the loop below is unrolled by two so that each step's LDS buffer
-  // (BUF) is a compile-time constant and the LDS addresses fold into the instructions.
-  auto step = [&](auto buf_tag, int t) {
-    constexpr int BUF = decltype(buf_tag)::value;
+  // Products and softmax of tile t from the LDS tiles kb (K) and vb (V^T).
+  auto tile_step = [&](const char* kb, const char* vb, int t) __attribute__((always_inline)) {
     const int j0 = t * kBC;
-    const bool more = t + 1 < nt;
-    if (more) stage_load<D>(stg, kh, vth, N, p.ldv, j0 + kBC, koff, voff, vkey, j0 + 2 * kBC > N);
-    const char* kb = kbuf[BUF];
-    const char* vb = vbuf[BUF];
 
     // S^T = K Q^T for the two 32-key blocks
     f32x16 s[2];
@@ -337,13 +337,35 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
       const int f = 32 * mt + l32;
       oacc[mt] = mma(read32<kBC>(vb, f, 2 * hl, vswz(f)), pb, oacc[mt]);
     }
+  };
 
+  // One pipelined tile step; the loop below is unrolled by two so that each step's
+  // LDS buffer (BUF) is a compile-time constant and the LDS addresses fold into the
+  // instructions.
+  auto step = [&](auto buf_tag, int t) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const int j0 = t * kBC;
+    const bool more = t + 1 < nt;
+    if (more) stage_load<D>(stg, kh, vth, N, p.ldv, j0 + kBC, koff, voff, vkey, j0 + 2 * kBC > N);
+    tile_step(kbuf[BUF], vbuf[BUF], t);
     if (more) stage_store<D>(stg, kbuf[BUF ^ 1], vbuf[BUF ^ 1], tid);
     __syncthreads();
   };
-  for (int t = 0; t < nt; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < nt) step(std::integral_constant<int, 1>{}, t + 1);
+  if (REF) {
+    for (int t = 0; t < nt; ++t) {
+      if (t > 0) {
+        __syncthreads();
+        stage_load<D>(stg, kh, vth, N, p.ldv, t * kBC, koff, voff, vkey, (t + 1) * kBC > N);
+        stage_store<D>(stg, kbuf[0], vbuf[0], tid);
+        __syncthreads();
+      }
+      tile_step(kbuf[0], vbuf[0], t);
+    }
+  } else {
+    for (int t = 0; t < nt; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < nt) step(std::integral_constant<int, 1>{}, t + 1);
+    }
   }
 
 

@@ -11,13 +11,14 @@
 #include <atomic>
 #include <mutex>
 #include <stdarg.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
 #include "attn_fwd.h"
 #include "attn_host.h"
-#include "attn_fwd_kernel.h"
+#include "attn_fwd_launch.h"
 #include "exp2_poly.h"
 
 namespace attn_host {
@@ -41,21 +42,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace attn_host
 
-namespace {
+namespace attn_launch {
 
-using attn_host::fail;
-using attn_host::g_last_error;
-using attn_host::overlaps;
-
-// Tile configuration: 8 wavefronts (256 query rows) per workgroup, BC keys per KV tile.
-constexpr int kWaves = 8;
-constexpr int kRows = 32 * kWaves;  // query rows per workgroup
-template <int D> struct Cfg;
-template <> struct Cfg<128> { static constexpr int BC = 64; };
-template <> struct Cfg<64> { static constexpr int BC = 64; };
-
-// Compute units per XCD of the current device (8 XCDs per MI355X), cached per
-// device; 0 if the runtime cannot tell (then every tile gets its own workgroup).
 int cus_per_xcd() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -70,63 +58,25 @@ int cus_per_xcd() {
   return v;
 }
 
-template <int D, bool CAUSAL, bool OF32, int POLY8, bool NEG>
-const void* kernel_fn(bool varlen) {
-  return varlen ? reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, OF32, POLY8, NEG, true>)
-                : reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, OF32, POLY8, NEG, false>);
-}
+}  // namespace attn_launch
 
-template <int D, bool CAUSAL, bool OF32, int POLY8>
-hipError_t launch(const attn::Params& p, bool neg, bool varlen, hipStream_t stream) {
-  // hipLaunchKernel reports this launch's own error (no sticky state from other calls).
-  // A negative scale flips the row maximum of s*c into c * min(s): separate instantiation.
-  // One workgroup per compute unit walks its XCD's tile range, so the next tile's
-  // loads overlap the current tile's epilogue (causal: in a length-balanced order).
-  int per_wg_xcd = p.per_xcd;
-  const int slots = cus_per_xcd();
-  if (slots > 0 && slots < per_wg_xcd) per_wg_xcd = slots;
-  const dim3 grid(per_wg_xcd * 8), block(64 * kWaves);
-  void* args[] = {const_cast<attn::Params*>(&p)};
-  const void* fn = neg ? kernel_fn<D, CAUSAL, OF32, POLY8, true>(varlen) : kernel_fn<D, CAUSAL, OF32, POLY8, false>(varlen);
-  return hipLaunchKernel(fn, grid, block, args, 0, stream);
-}
+namespace {
 
-template <int D, bool CAUSAL, bool OF32>
-hipError_t launch_poly(const attn::Params& p, int poly8, bool neg, bool varlen, hipStream_t s) {
-  switch (poly8) {
-    case 0: return launch<D, CAUSAL, OF32, 0>(p, neg, varlen, s);
-    case 4: return launch<D, CAUSAL, OF32, 4>(p, neg, varlen, s);
-    default: return launch<D, CAUSAL, OF32, 8>(p, neg, varlen, s);
-  }
-}
+using attn_host::fail;
+using attn_host::g_last_error;
+using attn_host::overlaps;
 
-template <int D>
-hipError_t launch_d(const attn::Params& p, bool causal, bool of32, int poly8, bool neg, bool varlen, hipStream_t s) {
-  if (causal)
-    return of32 ? launch_poly<D, true, true>(p, poly8, neg, varlen, s)
-                : launch_poly<D, true, false>(p, poly8, neg, varlen, s);
-  return of32 ? launch_poly<D, false, true>(p, poly8, neg, varlen, s)
-              : launch_poly<D, false, false>(p, poly8, neg, varlen, s);
-}
+using attn_launch::Cfg;
+using attn_launch::kRows;
 
-// Split keys: the partial kernel (fp32 partial O and LSE per unit into the
-// workspace), then the merge kernel, on one stream.
-template <int D, bool CAUSAL>
-hipError_t launch_split(const attn::Params& p, bool neg, bool of32, int rows_total, hipStream_t stream) {
-  int per_wg_xcd = p.per_xcd;
-  const int slots = cus_per_xcd();
-  if (slots > 0 && slots < per_wg_xcd) per_wg_xcd = slots;
-  void* args[] = {const_cast<attn::Params*>(&p)};
-  const void* fn =
-      neg ? reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, true, 0, true, false, true>)
-          : reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, true, 0, false, false, true>);
-  hipError_t e = hipLaunchKernel(fn, dim3(per_wg_xcd * 8), dim3(64 * kWaves), args, 0, stream);
-  if (e != hipSuccess) return e;
-  int split_keys = p.split_tiles * Cfg<D>::BC;
-  void* margs[] = {const_cast<attn::Params*>(&p), &rows_total, &split_keys};
-  const void* mfn = of32 ? reinterpret_cast<const void*>(&attn::attn_merge_kernel<D, CAUSAL, true>)
-                         : reinterpret_cast<const void*>(&attn::attn_merge_kernel<D, CAUSAL, false>);
-  return hipLaunchKernel(mfn, dim3((rows_total + 3) / 4), dim3(256), margs, 0, stream);
+hipError_t launch_any(const attn::Params& p, int d, bool causal, bool of32, int poly8, bool neg, bool varlen,
+                      bool ref, hipStream_t s) {
+  using attn_launch::launch_dense;
+  if (d == 128)
+    return causal ? launch_dense<128, true>(p, of32, poly8, neg, varlen, ref, s)
+                  : launch_dense<128, false>(p, of32, poly8, neg, varlen, ref, s);
+  return causal ? launch_dense<64, true>(p, of32, poly8, neg, varlen, ref, s)
+                : launch_dense<64, false>(p, of32, poly8, neg, varlen, ref, s);
 }
 
 // One call, dense ([B][H][N][d]) or packed (varlen: [H][total][d] with cu_seqlens).
@@ -150,9 +100,13 @@ attn_status_t validate(const Problem& P, const attn_fwd_opts* opts, attn_fwd_opt
   *work = false;
   attn_fwd_opts_init(def);
   if (opts) {
-    if (opts->struct_size < sizeof(attn_fwd_opts))
-      return fail(ATTN_ERR_OPTS, "opts->struct_size %zu < %zu", opts->struct_size, sizeof(attn_fwd_opts));
-    *def = *opts;
+    // callers built against a header without `schedule` pass the shorter struct
+    // and get the default schedule
+    const size_t base = offsetof(attn_fwd_opts, schedule);
+    if (opts->struct_size < base)
+      return fail(ATTN_ERR_OPTS, "opts->struct_size %zu < %zu", opts->struct_size, base);
+    memcpy(def, opts, opts->struct_size < sizeof(attn_fwd_opts) ? opts->struct_size : sizeof(attn_fwd_opts));
+    def->struct_size = sizeof(attn_fwd_opts);
   }
   const int B = P.B, H = P.H, Hkv = P.Hkv, N = P.N, d = P.d;
   if (B < 0 || H < 0 || N < 0) return fail(ATTN_ERR_DIM, "negative size B=%d H=%d N=%d", B, H, N);
@@ -167,6 +121,10 @@ attn_status_t validate(const Problem& P, const attn_fwd_opts* opts, attn_fwd_opt
     return fail(ATTN_ERR_UNSUPPORTED, "exp2_poly_eighths %d (supported: 0, 4, 8)", def->exp2_poly_eighths);
   if (def->o_dtype != ATTN_O_BF16 && def->o_dtype != ATTN_O_F32)
     return fail(ATTN_ERR_UNSUPPORTED, "o_dtype %d", def->o_dtype);
+  if (def->schedule != ATTN_SCHEDULE_PIPELINED && def->schedule != ATTN_SCHEDULE_REFERENCE)
+    return fail(ATTN_ERR_OPTS, "schedule %d", def->schedule);
+  if (def->schedule == ATTN_SCHEDULE_REFERENCE && (def->exp2_poly_eighths != 0 || P.scale < 0.f))
+    return fail(ATTN_ERR_UNSUPPORTED, "the reference schedule needs exp2_poly_eighths 0 and scale >= 0");
   // longest sequence a query tile walk has to cover
   const int64_t seq = P.varlen ? (P.max_seqlen < N ? P.max_seqlen : N) : N;
   if ((int64_t)B * H * seq == 0) return ATTN_OK;  // empty: nothing to do
@@ -247,11 +205,11 @@ attn_status_t run(const Problem& P, int causal, const attn_fwd_opts* opts, void*
   p.ws_lse = nullptr;
   p.split_stride = 0;
 
+  const bool ref = o2.schedule == ATTN_SCHEDULE_REFERENCE;
   const bool of32 = o2.o_dtype == ATTN_O_F32;
   const bool neg = P.scale < 0.f;
   const hipError_t err =
-      P.d == 128 ? launch_d<128>(p, causal != 0, of32, o2.exp2_poly_eighths, neg, P.varlen, (hipStream_t)stream)
-                 : launch_d<64>(p, causal != 0, of32, o2.exp2_poly_eighths, neg, P.varlen, (hipStream_t)stream);
+      launch_any(p, P.d, causal != 0, of32, o2.exp2_poly_eighths, neg, P.varlen, ref, (hipStream_t)stream);
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
   return ATTN_OK;
 }
@@ -265,7 +223,7 @@ void split_shape(int B, int H, int N, int d, int n_splits, int* splits, int* spl
   int s = n_splits;
   if (s <= 0) {
     const int64_t units = (int64_t)B * H * ((N + kRows - 1) / kRows);
-    const int cus = cus_per_xcd() > 0 ? cus_per_xcd() * 8 : 256;
+    const int cus = attn_launch::cus_per_xcd() > 0 ? attn_launch::cus_per_xcd() * 8 : 256;
     s = units >= cus ? 1 : (int)((cus + units - 1) / units);
   }
   s = s < 1 ? 1 : (s > key_tiles ? key_tiles : s);
@@ -332,14 +290,17 @@ attn_status_t run_split(const Problem& P, int causal, int n_splits, void* ws, si
   p.ws_o = (float*)ws;
   p.ws_lse = (float*)((char*)ws + (splits * (size_t)rows * P.d * 4 + 255) / 256 * 256);
   p.split_stride = (size_t)rows;
+  const bool ref = o2.schedule == ATTN_SCHEDULE_REFERENCE;
   const bool of32 = o2.o_dtype == ATTN_O_F32;
   const bool neg = P.scale < 0.f;
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (P.d == 128)
-    e = causal ? launch_split<128, true>(p, neg, of32, (int)rows, s) : launch_split<128, false>(p, neg, of32, (int)rows, s);
+    e = causal ? attn_launch::launch_split<128, true>(p, neg, of32, (int)rows, ref, s)
+               : attn_launch::launch_split<128, false>(p, neg, of32, (int)rows, ref, s);
   else
-    e = causal ? launch_split<64, true>(p, neg, of32, (int)rows, s) : launch_split<64, false>(p, neg, of32, (int)rows, s);
+    e = causal ? attn_launch::launch_split<64, true>(p, neg, of32, (int)rows, ref, s)
+               : attn_launch::launch_split<64, false>(p, neg, of32, (int)rows, ref, s);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ATTN_OK;
 }
@@ -475,7 +436,7 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, flo
   return attn_fwd_ex(q, k, v, o, lse, B, H, N, d, causal, scale, nullptr, stream);
 }
 
-const char* attn_status_str(attn_status_t s) {
+const char* attn_status_str(int s) {
   switch (s) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "null pointer";

@@ -1,0 +1,11 @@
+// attn_fwd_d64_causal.hip - instantiations of the attention forward kernel and its launches
+// for head dim 64, causal mask (one translation unit per head dim and mask,
+// compiled in parallel).
+#include "attn_fwd_launch_impl.h"
+
+namespace attn_launch {
+
+template hipError_t launch_dense<64, true>(const attn::Params&, bool, int, bool, bool, bool, hipStream_t);
+template hipError_t launch_split<64, true>(const attn::Params&, bool, bool, int, bool, hipStream_t);
+
+}  // namespace attn_launch

@@ -413,6 +413,15 @@ struct VSplit {
   static_assert(4 % MT == 0, "head of whole k-steps");
 };
 
+// PV operand of value-feature block mt for k-step ks of a V head or tail buffer:
+// two transpose reads (see v_offsets).
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand(const char* buf, int ks, int mt, const int (&voffs)[D / 32]) {
+  const s16x4 lo = v_col4<D>(buf + voffs[mt], 16 * ks);
+  const s16x4 hi = v_col4<D>(buf + voffs[mt], 16 * ks + 8);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Number of LDS reads issued after PV product (g, mt) of matrix_phase.
 template <int D, int BC, int KA>
 __host__ __device__ constexpr int pv_reads(int g, int mt) {
@@ -458,11 +467,7 @@ __device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 3
   __builtin_amdgcn_s_setprio(1);
   bf16x8 kf[NQK];
   bf16x8 vf[NKS][MT];
-  auto vfrag = [&](const char* buf, int ks, int mt) {  // ks: k-step within the buffer
-    const s16x4 lo = v_col4<D>(buf + voffs[mt], 16 * ks);
-    const s16x4 hi = v_col4<D>(buf + voffs[mt], 16 * ks + 8);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
+  auto vfrag = [&](const char* buf, int ks, int mt) { return v_operand<D>(buf, ks, mt, voffs); };
   auto kread = [&](int f) { kf[f] = k_frag_at<D>(kb, koffs[f % KK], f / KK); };
 #pragma unroll
   for (int g = 0; g < HKS; ++g)
@@ -501,13 +506,39 @@ __device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 3
   __builtin_amdgcn_s_setprio(0);
 }
 
+// O^T += V^T P^T of the reference schedule: the PV products of matrix_phase in
+// the same order (k-step by k-step, value-feature block mt within), with every
+// operand read from the head and tail buffers beforehand.
+template <int D, int BC>
+__device__ __forceinline__ void pv_reference(RowState<D>& st, const bf16x8 (&pb)[BC / 32][2], const char* vhd,
+                                             const char* vtl, const int (&voffs)[D / 32]) {
+  constexpr int NKS = BC / 16, HKS = VSplit<D>::HKS, MT = D / 32;
+  bf16x8 vf[NKS][MT];
+#pragma unroll
+  for (int g = 0; g < NKS; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) vf[g][mt] = v_operand<D>(g < HKS ? vhd : vtl, g < HKS ? g : g - HKS, mt, voffs);
+#pragma unroll
+  for (int g = 0; g < NKS; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      st.oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g][mt], pb[g / 2][g % 2], st.oacc[mt], 0, 0, 0);
+}
+
 // VARLEN: packed variable-length batches. q and o are [H][total][D], k and v
 // [Hkv][total][D], lse [H][total]; sequence b owns tokens cu[b] .. cu[b+1]-1 of
 // every head and attends only to itself (causal positions counted from its
 // first token). Each tile reads its sequence's bounds; the buffer resources end
 // at the sequence's last row, so no load crosses into the next sequence.
 // SPLIT: split keys (see Params); requires OF32 (the partial results are fp32).
-template <int D, int BC, bool CAUSAL, bool OF32, int POLY8, bool NEG, bool VARLEN, bool SPLIT = false>
+// REF: the reference schedule, for race checking: the same arithmetic in the
+// same order (each wavefront's QK, softmax and PV products of every tile), with
+// one buffer per tensor, every tile load issued after a barrier that follows
+// all reads of the previous tile and waited for (vmcnt(0) and a barrier) before
+// any read, and no phase offset between the wavefront groups. Its results must
+// equal the pipelined schedule's bit for bit.
+template <int D, int BC, bool CAUSAL, bool OF32, int POLY8, bool NEG, bool VARLEN, bool SPLIT = false,
+          bool REF = false>
 __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   constexpr int NW = 8;            // wavefronts per workgroup (2 per SIMD)
   constexpr int BR = 32 * NW;      // query rows per workgroup
@@ -636,7 +667,8 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     const size_t kvoff = kvhead + (SPLIT ? (size_t)t.kb * BC * D : 0);
     const int nkv = n - (SPLIT ? t.kb * BC : 0);
     // K_0, K_1 (group A) and V_0, V_1's head (group B); n_tiles >= 1
-    if (grp == 0) {
+    if (REF) {
+    } else if (grp == 0) {
       load_tile<D, BC, 4>(koff, p.k + kvoff, nkv, 0, kbuf0, wave & 3, true);
       load_tile<D, BC, 4>(koff, p.k + kvoff, nkv, BC, kbuf1, wave & 3, t.n_tiles > 1);
     } else {
@@ -687,6 +719,25 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   f32x16 s[NC];
   bf16x8 va[VSplit<D>::HKS][MT];  // PV operands of the head of the V tile the next matrix phase multiplies
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's tile and Q loads landed
+  if (REF) {
+    // reference schedule: one buffer per tensor, full waits, no phase offset
+    for (int k = 0; k < n_tiles; ++k) {
+      __syncthreads();  // every wavefront's reads of the previous tile are complete
+      if (grp == 0) {
+        load_tile<D, BC, 4>(koff, kh, Nkv, k * BC, kbuf0, wave & 3, true);
+      } else {
+        load_tile<D, VHR, 4>(vhoff, vh, Nkv, k * BC, vhd0, wave & 3, true);
+        load_tile<D, VTR, 4>(vtoff, vh, Nkv, k * BC + VHR, vtl0, wave & 3, true);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, s, koffs);
+      bf16x8 pb[NC][2];
+      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau);
+      pv_reference<D, BC>(st, pb, vhd0, vtl0, voffs);
+    }
+    __syncthreads();
+  } else {
   __syncthreads();                      // K_0, K_1, V_0, V_1's head resident for every wavefront
 #pragma unroll
   for (int g = 0; g < VSplit<D>::HKS; ++g)
@@ -754,6 +805,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     }
     if (k < n_tiles) pair(k, kbuf1, vhd1, vtl0);
   }
+  }  // pipelined schedule
 
   // Every wavefront has passed the last barrier, so no LDS tile and no Q
   // register is read again: the next tile's loads can go out now and land

@@ -68,6 +68,14 @@ attn_status_t attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o
                            int N, int d, int causal, float scale, float q_scale, float k_scale,
                            float v_scale, float tau, void* stream);
 
+/* attn_fwd_fp8 with a kernel schedule: ATTN_SCHEDULE_PIPELINED (what attn_fwd_fp8
+ * runs) or ATTN_SCHEDULE_REFERENCE, a race check that loads each tile between two
+ * block-wide barriers and gives bitwise the same results, several times slower.
+ * Another value returns ATTN_ERR_OPTS (after the checks of attn_fwd_fp8). */
+attn_status_t attn_fwd_fp8_ex(const void* q, const void* k, const void* vt, void* o, float* lse, int B, int H,
+                              int N, int d, int causal, float scale, float q_scale, float k_scale,
+                              float v_scale, float tau, int schedule, void* stream);
+
 /* Host-only argument check of attn_fwd_fp8 (never touches the device). */
 attn_status_t attn_fwd_fp8_check(const void* q, const void* k, const void* vt, const void* o,
                                  const float* lse, int B, int H, int N, int d, int causal, float scale,

@@ -50,8 +50,9 @@ extern "C" {
  * 5: adds attn_fwd_splitkv and attn_fwd_splitkv_workspace_size (split keys).
  * 6: adds attn_fwd_fp8 and attn_fwd_fp8_check (FP8 e4m3 inputs, declared in attn_fp8.h).
  * 7: adds attn_bwd_varlen and attn_bwd_varlen_check (declared in attn_bwd.h).
- * 8: adds attn_fwd_splitkv_noalloc. */
-#define ATTN_ABI_VERSION 8
+ * 8: adds attn_fwd_splitkv_noalloc.
+ * 9: adds the schedule option (attn_fwd_opts.schedule) and attn_fwd_fp8_ex. */
+#define ATTN_ABI_VERSION 9
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -62,11 +63,18 @@ typedef enum attn_status {
   ATTN_ERR_SCALE = 5,       /* scale is not finite */
   ATTN_ERR_ALIAS = 6,       /* o or lse overlaps an input, or o overlaps lse */
   ATTN_ERR_HIP = 7,         /* the kernel launch failed; details in attn_last_error() */
-  ATTN_ERR_OPTS = 8         /* opts->struct_size too small, or tau out of [0, 64] */
+  ATTN_ERR_OPTS = 8         /* opts->struct_size too small, tau out of [0, 64], or an unknown schedule */
 } attn_status_t;
 
 /* Output element type of o. */
 enum { ATTN_O_BF16 = 0, ATTN_O_F32 = 1 };
+
+/* Kernel schedule: the production ping-pong pipeline, or a reference schedule
+ * that computes the same tiles in the same arithmetic order with every load
+ * fenced by a block-wide barrier before its first use (no tile is in flight
+ * while another is read). The two give bitwise-identical results; a difference
+ * shows a synchronisation error in the pipeline. */
+enum { ATTN_SCHEDULE_PIPELINED = 0, ATTN_SCHEDULE_REFERENCE = 1 };
 
 /*
  * Options for attn_fwd_ex. Initialise with attn_fwd_opts_init, then set fields.
@@ -88,6 +96,11 @@ enum { ATTN_O_BF16 = 0, ATTN_O_F32 = 1 };
  * rescale_count: optional DEVICE pointer to int32 [B][H][N]; when not NULL the
  *   kernel stores, per query row, the number of rescales after the row's first
  *   tile (instrumentation; not part of the result). Must not overlap any tensor.
+ * schedule: ATTN_SCHEDULE_PIPELINED (default) or ATTN_SCHEDULE_REFERENCE (a race
+ *   check, several times slower; needs exp2_poly_eighths 0 and scale >= 0, else
+ *   ATTN_ERR_UNSUPPORTED; other values: ATTN_ERR_OPTS). Callers built against
+ *   ABI 8, whose struct ends before this field, pass the shorter struct_size and
+ *   get the default.
  */
 typedef struct attn_fwd_opts {
   size_t struct_size; /* sizeof(attn_fwd_opts) */
@@ -95,9 +108,11 @@ typedef struct attn_fwd_opts {
   int exp2_poly_eighths;
   int o_dtype;
   int* rescale_count;
+  int schedule;
 } attn_fwd_opts;
 
-/* Fill *opts with the defaults (struct_size set, tau 8, no polynomial, bf16 O). */
+/* Fill *opts with the defaults (struct_size set, tau 8, no polynomial, bf16 O,
+ * pipelined schedule). */
 void attn_fwd_opts_init(attn_fwd_opts* opts);
 
 /*
@@ -269,8 +284,9 @@ attn_status_t attn_fwd_splitkv_noalloc(const void* q, const void* k, const void*
  * ATTN_ERR_UNSUPPORTED for a head dim other than 64 or 128, or ATTN_ERR_NULL. */
 attn_status_t attn_fwd_tile_shape(int d, int* query_rows, int* key_cols);
 
-/* Static text for a status code. */
-const char* attn_status_str(attn_status_t status);
+/* Static text for a status code. Takes any int (an attn_status_t converts
+ * implicitly); a value that is not a status gives "unknown status". */
+const char* attn_status_str(int status);
 
 /* Text of the last error raised on the calling thread ("" if none). */
 const char* attn_last_error(void);

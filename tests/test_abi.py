@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(bnd.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.attn_abi_version() == bnd.ABI_VERSION == 8
+    assert lib.attn_abi_version() == bnd.ABI_VERSION == 9
 
 
 def check(*args, **kw):
@@ -94,6 +94,30 @@ def test_options():
     assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(rescale_count=L + 2)) == 4
     assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(rescale_count=L)) == 6
     assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(rescale_count=6 * GB)) == bnd.ATTN_OK
+
+
+def test_schedule_option():
+    ref = bnd.SCHEDULE_REFERENCE
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(schedule=ref)) == bnd.ATTN_OK
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 1, 0.0, bnd.make_opts(schedule=ref, o_dtype=1)) == bnd.ATTN_OK
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(schedule=2)) == 8
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(schedule=-1)) == 8
+    # the reference schedule covers the hardware exponential and scale >= 0 only
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, bnd.make_opts(schedule=ref, poly_eighths=4)) == 3
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, -1.0, bnd.make_opts(schedule=ref)) == 3
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, -1.0, bnd.make_opts()) == bnd.ATTN_OK
+
+
+def test_options_struct_of_the_previous_abi():
+    # a caller built against ABI 8 passes the struct without `schedule` (32 bytes on
+    # LP64): the library must not read the field and must use the default
+    base = ctypes.sizeof(bnd.AttnFwdOpts) - 8
+    assert bnd.AttnFwdOpts.schedule.offset == base == 32
+    old = bnd.make_opts(schedule=7)
+    old.struct_size = base
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, old) == bnd.ATTN_OK
+    old.struct_size = base - 1
+    assert check(Q, K, V, O, L, 1, 1, 8, 64, 0, 1.0, old) == 8
 
 
 def test_tile_shape():
@@ -278,6 +302,15 @@ def test_fp8_valid_and_empty():
     assert fp8_check(N=77, d=64, causal=1, tau=0.0) == bnd.ATTN_OK
     assert fp8_check(q=None, k=None, vt=None, o=None, lse=None, N=0) == bnd.ATTN_OK
     assert bnd.attn_fwd_fp8(None, None, None, None, None, 0, 1, 16, 64, 0, 1.0, 1.0, 1.0, 1.0, 8.0, None) == bnd.ATTN_OK
+    for sched in (bnd.SCHEDULE_PIPELINED, bnd.SCHEDULE_REFERENCE):
+        assert bnd.attn_fwd_fp8_ex(None, None, None, None, None, 0, 1, 16, 64, 0, 1.0, 1.0, 1.0, 1.0, 8.0, sched,
+                                   None) == bnd.ATTN_OK
+    # an unknown schedule is an error even where nothing would be launched
+    assert bnd.attn_fwd_fp8_ex(None, None, None, None, None, 0, 1, 16, 64, 0, 1.0, 1.0, 1.0, 1.0, 8.0, 2,
+                               None) == 8
+    # argument errors come first
+    assert bnd.attn_fwd_fp8_ex(None, None, None, None, None, 1, 1, 16, 96, 0, 1.0, 1.0, 1.0, 1.0, 8.0, 2,
+                               None) == 3
 
 
 @pytest.mark.parametrize("patch,code", [
