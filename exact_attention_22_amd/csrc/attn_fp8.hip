@@ -97,6 +97,7 @@ attn_status_t attn_fwd_fp8_ex(const void* q, const void* k, const void* vt, void
   p.c = scale * q_scale * k_scale * 1.44269504088896341f;
   p.ov = v_scale;
   p.tau = tau;
+  p.psum_thr = (1.f - 0x1p-10f) * exp2f(tau);  // P above 2^tau puts a partial sum above this
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (d == 128)

@@ -23,15 +23,17 @@
 //   S^T = K . Q^T: register byte s of lane half h is feature 64*m + 32*h + s
 //     for the product over features 64*m .. 64*m+63;
 //   O^T += V^T . P^T: register byte s = 16*c + r of lane half h is key
-//     32*c + 8*(r/4) + 4*h + r%4 of the 64-key tile - exactly the keys whose
-//     scores lane l holds in register r of the S accumulator of key block c, so
-//     P^T goes from the first product's output to the second one's B operand
-//     without leaving the lane.
-// The A operand of the second product (value feature f, those 32 keys) is one
-// contiguous 32-byte run of the transposed V tile in LDS, because the tile's
-// columns are stored permuted: key 32c + 8a + 4h + b sits at column
-// 32h + 16c + 4a + b. V is handed over transposed, [B][H][d][ldv]
-// (ldv = N rounded up to 16), so the kernel's loads of V^T rows are 16-byte
+//     32*h + 16*c + r of the 64-key tile.
+// The first product's output row 32*c + 8*(r/4) + 4*h + r%4 (register r of
+// accumulator c in lane half h) is the K tile's row of that index, and the K
+// tile holds its keys permuted: row 32*c + 8*a + 4*h + b holds key
+// 32*h + 16*c + 4*a + b. Register r of accumulator c in lane half h is then
+// the score of key 32*h + 16*c + r, exactly the key of byte 16*c + r of the
+// second product's B operand: P^T goes from the first product's output to the
+// second one's B operand without leaving the lane, and the A operand of the
+// second product (value feature f, keys 32*h .. 32*h+31) is one contiguous
+// 32-byte run of the transposed V tile in key order. V is handed over
+// transposed, [B][H][d][ldv] (ldv = N rounded up to 16), so its tile rows are
 // runs of consecutive keys.
 //
 // P is rounded to e4m3 (v_cvt_pk_fp8_f32, round to nearest even) before the
@@ -40,16 +42,20 @@
 //
 // Layout: one workgroup = 4 wavefronts = 128 query rows of one (b, h), one
 // query row per lane (the S and O accumulators hold one query column per
-// lane), Q in registers. K and V^T tiles of 64 keys are staged through
-// registers into double-buffered LDS, one barrier per tile: the global loads of
-// tile t+1 are issued before tile t's products and written to the other buffer
-// after them. Two workgroups share a compute unit.
+// lane), Q in registers; two workgroups share a compute unit at d = 128. K and
+// V^T tiles of 64 keys go from memory straight into LDS (buffer loads with the
+// LDS as destination, 16 bytes per lane), two tiles ahead of the products,
+// into three buffers: step t waits for tile t's loads (issued two steps
+// earlier), passes one barrier, issues tile t+2's loads into the buffer tile
+// t-1 used, and computes tile t. The per-lane global addresses place each
+// 16-byte chunk at its swizzled LDS position, so the tiles need no register
+// staging and no LDS stores.
 //
 // REF = true instantiates a reference schedule for race checks: each tile is
-// loaded and stored to LDS between two block-wide barriers and only then read,
-// with one buffer and no load in flight during the products. The arithmetic is
-// the same instructions in the same order, so its results are bitwise equal to
-// the pipelined schedule's.
+// loaded into one buffer between two block-wide barriers, with every load
+// complete before the second, and only then read. The arithmetic is the same
+// instructions in the same order, so its results are bitwise equal to the
+// pipelined schedule's.
 #ifndef ATTN_FP8_KERNEL_H
 #define ATTN_FP8_KERNEL_H
 
@@ -91,6 +97,7 @@ struct Fp8Params {
   float c;            // scale * q_scale * k_scale * log2(e) (> 0)
   float ov;           // v_scale
   float tau;          // rescale threshold, log2 units, in [0, 8]
+  float psum_thr;     // 2^tau * (1 - 2^-10): a lane's partial sum above it may hide a P above 2^tau
 };
 
 // One matrix instruction: 32x32 fp32 += A (32 x 64 e4m3) . B (64 x 32 e4m3).
@@ -100,10 +107,9 @@ __device__ __forceinline__ f32x16 mma(const i32x8& a, const i32x8& b, const f32x
 
 // 16-byte chunk swizzles of the LDS tiles (chunk c of row r is stored at chunk
 // position c ^ swz(r)). The reads take one logical chunk of 16 consecutive
-// rows per 16 lanes (or of 8 rows per 8 lanes); the V^T writes put 8-byte runs
-// of 4 or 8 consecutive rows at two chunk positions. The swizzles below make
-// all of these hit distinct banks whether the LDS serves 128 or 256 bytes per
-// pass (checked on the CPU against both bank models).
+// rows per 16 lanes (or of 8 rows per 8 lanes); the swizzles below make them
+// hit distinct banks whether the LDS serves 128 or 256 bytes per pass (checked
+// on the CPU against both bank models). The tile loads write whole 1 KiB runs.
 // 128-byte rows (K at D = 128): chunk bits 0..2 from the row, bit 0 also from row bit 3.
 // 64-byte rows (V^T, and K at D = 64): with a, b, c = row bits 1, 2, 3:
 //   swz = 2 * (a ^ b) + (b ^ c).
@@ -122,16 +128,7 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Per-thread staging of one tile: K rows (D bytes each) and V^T rows (64 keys each).
-template <int D>
-struct Stage {
-  static constexpr int NT = 64 * Shape<D>::NW;  // threads
-  static constexpr int KCH = kBC * D / 16 / NT;  // 16-byte K chunks per thread
-  static constexpr int VCH = D * kBC / 16 / NT;  // 16-byte V^T chunks per thread
-  static_assert(KCH * NT * 16 == kBC * D && VCH * NT * 16 == D * kBC, "tile split");
-  u32x4 kc[KCH];
-  u32x4 vc[VCH];
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Buffer resource over `bytes` bytes at `base` (raw loads past the end return zeros;
 // DATA_FORMAT = 32-bit in the third descriptor word, as raw loads require).
@@ -139,57 +136,101 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Loads of the tile at key j0. K: a resource starting at row j0 and ending at row N,
-// so rows past N read as zeros. V^T: a resource over the rest of the head from
-// column j0; the per-thread offsets (koff, voff) are fixed for the whole kernel.
-// Chunks at or past column N (only in the last tile) may hold padding or the next
-// row's keys; `edge` zeroes those bytes (N - key bytes of the chunk are real keys).
+// Direct-to-LDS loads of one 64-key tile: each instruction writes 1 KiB (16 bytes
+// per lane, lane l at byte 16 l); K needs 64*D/1024 instructions, V^T as many.
 template <int D>
-__device__ __forceinline__ void stage_load(Stage<D>& st, const uint8_t* kh, const uint8_t* vth, int N, int ldv, int j0,
-                                           const uint32_t (&koff)[Stage<D>::KCH],
-                                           const uint32_t (&voff)[Stage<D>::VCH], int vkey, bool edge) {
-  const __amdgpu_buffer_rsrc_t kr = rsrc(kh + (size_t)j0 * D, (uint32_t)(N - j0) * D);
-  const __amdgpu_buffer_rsrc_t vr = rsrc(vth + j0, (uint32_t)(D * ldv - j0));
+struct TileLoads {
+  static constexpr int NW = Shape<D>::NW;
+  static constexpr int KI = kBC * D / 1024;  // K instructions per tile
+  static constexpr int VI = D * kBC / 1024;  // V^T instructions per tile
+  static constexpr int KPW = KI / NW;        // per wavefront
+  static constexpr int VPW = VI / NW;
+  static constexpr int PW = KPW + VPW;
+  static_assert(KPW * NW == KI && VPW * NW == VI, "tile split");
+};
+
+// Byte offsets, relative to the tile's first key, of this lane's 16-byte chunks.
+// K instruction i of wavefront w writes LDS bytes 1024 (i NW + w) .. +1023: lane
+// l's chunk is tile row R = (that byte + 16 l) / D at chunk position p, i.e.
+// logical chunk p ^ kswz(R) of the key the row holds, 32h + 16c + 4a + b for
+// R = 32c + 8a + 4h + b. V^T: row F (feature) at chunk position p holds logical
+// chunk p ^ vswz(F), keys 16 (p ^ vswz(F)) .. +15 of the tile.
+template <int D>
+__device__ __forceinline__ void load_offsets(uint32_t* koff, uint32_t* voff, int wave, int lane, int ldv) {
+  using L = TileLoads<D>;
 #pragma unroll
-  for (int i = 0; i < Stage<D>::KCH; ++i)
-    st.kc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], 0, 0));
+  for (int i = 0; i < L::KPW; ++i) {
+    const int byte = 1024 * (i * L::NW + wave) + 16 * lane;
+    const int R = byte / D, pos = (byte % D) / 16;
+    const int c = R >> 5, a = (R >> 3) & 3, h = (R >> 2) & 1, b = R & 3;
+    const int key = 32 * h + 16 * c + 4 * a + b;
+    koff[i] = (uint32_t)(key * D + 16 * (pos ^ kswz<D>(R)));
+  }
 #pragma unroll
-  for (int i = 0; i < Stage<D>::VCH; ++i)
-    st.vc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0));
-  if (edge) {
-    const int valid = N - (j0 + vkey);  // real keys in this thread's V^T chunks (same column for every i)
-#pragma unroll
-    for (int i = 0; i < Stage<D>::VCH; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int keep = valid - 4 * e;  // bytes kept in word e
-        const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u);
-        st.vc[i][e] &= m;
-      }
+  for (int i = 0; i < L::VPW; ++i) {
+    const int byte = 1024 * (i * L::NW + wave) + 16 * lane;
+    const int F = byte / kBC, pos = (byte % kBC) / 16;
+    voff[i] = (uint32_t)(F * ldv + 16 * (pos ^ vswz(F)));
   }
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor words for `bytes` bytes at `base`, as __builtin_amdgcn_make_buffer_rsrc
+// builds them (stride 0; third word the record count; fourth word DATA_FORMAT = 32-bit).
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFF), (int)bytes, 0x00020000};
+}
+
+// One direct-to-LDS load: 16 bytes per lane from byte offset voff of the buffer,
+// lane l's bytes at LDS byte 16 l of the 1 KiB run at `lds`. Inline asm, because the
+// compiler's wait insertion cannot tell the three K (or V^T) buffers apart once
+// they are one LDS block and would make every LDS read wait for the loads in
+// flight into the other two buffers, which undoes the second tile of lookahead.
+// The kernel places every wait on these loads itself (wait_barrier); the asm has
+// no register outputs, and its address operands are read when it issues.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is clobbered on purpose: the kernel keeps nothing in it
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, const char* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(base), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Issue the loads of the tile at key j0 (live: the tile exists) into kb and vb.
+// K reads through a resource that ends at row N, so keys past N load as zeros;
+// V^T through one that ends at the head's end (the last tile's columns past N
+// hold padding or the next row's keys; the products never see them, see
+// mask_tail). A tile that does not exist loads zeros from an empty resource,
+// so every step issues the same number of loads.
 template <int D>
-__device__ __forceinline__ void stage_store(const Stage<D>& st, char* kb, char* vb, int tid) {
-  constexpr int KCPR = D / 16;
+__device__ __forceinline__ void load_tile(const uint32_t* koff, const uint32_t* voff, const uint8_t* kh,
+                                          const uint8_t* vth, int N, int ldv, int j0, bool live, char* kb, char* vb,
+                                          int wave) {
+  using L = TileLoads<D>;
+  const uint32_t krec = __builtin_amdgcn_readfirstlane(live ? (uint32_t)(N - j0) * D : 0u);
+  const uint32_t vrec = __builtin_amdgcn_readfirstlane(live ? (uint32_t)(D * ldv - j0) : 0u);
+  const i32x4 kr = rsrc_words(kh + (size_t)(live ? j0 : 0) * D, krec);
+  const i32x4 vr = rsrc_words(vth + (live ? j0 : 0), vrec);
 #pragma unroll
-  for (int i = 0; i < Stage<D>::KCH; ++i) {
-    const int id = tid + i * Stage<D>::NT;
-    const int row = id / KCPR, ch = id % KCPR;
-    *(u32x4*)(kb + row * D + ((ch ^ kswz<D>(row)) << 4)) = st.kc[i];
-  }
+  for (int i = 0; i < L::KPW; ++i) dma16(kr, koff[i], kb + 1024 * (i * L::NW + wave));
 #pragma unroll
-  for (int i = 0; i < Stage<D>::VCH; ++i) {
-    const int id = tid + i * Stage<D>::NT;
-    const int f = id >> 2, jc = id & 3;
-    // keys 16jc + e: e in {0..3, 8..11} (h = 0) and {4..7, 12..15} (h = 1); each set
-    // lands as 8 contiguous bytes at column 32h + 16*(jc/2) + 8*(jc%2)
-    const int c0 = 16 * (jc >> 1) + 8 * (jc & 1);
-    const int c1 = 32 + c0;
-    char* rowp = vb + f * kBC;
-    *(u32x2*)(rowp + (((c0 >> 4) ^ vswz(f)) << 4) + (c0 & 15)) = u32x2{st.vc[i][0], st.vc[i][2]};
-    *(u32x2*)(rowp + (((c1 >> 4) ^ vswz(f)) << 4) + (c1 & 15)) = u32x2{st.vc[i][1], st.vc[i][3]};
-  }
+  for (int i = 0; i < L::VPW; ++i) dma16(vr, voff[i], vb + 1024 * (i * L::NW + wave));
+}
+
+// Wait until at most n of this wavefront's vector-memory loads are outstanding
+// (and its LDS reads are done), then the workgroup barrier. Loads complete in
+// issue order, so n = the loads issued after the ones needed.
+template <int N_OUT>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N_OUT >= 0 && N_OUT < 16, "vmcnt field");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N_OUT);  // vmcnt(N_OUT), expcnt any, lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // 32 bytes of row `r` starting at logical chunk `ch` (two swizzled 16-byte chunks).
@@ -200,13 +241,26 @@ __device__ __forceinline__ i32x8 read32(const char* base, int r, int ch, int swz
   return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
 }
 
+// Zero the bytes of a V^T operand (keys 32 h .. 32 h + 31 of the tile) whose key is
+// at or past `valid` (the real keys of the last tile).
+__device__ __forceinline__ i32x8 mask_tail(i32x8 a, int h, int valid) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int keep = valid - 32 * h - 4 * w;  // real bytes in word w
+    const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u);
+    a[w] = (int)((uint32_t)a[w] & m);
+  }
+  return a;
+}
+
 template <int D, bool CAUSAL, bool REF = false>
 __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_fp8_kernel(const Fp8Params p) {
   constexpr int kRows = Shape<D>::ROWS;
   constexpr int MQ = D / 64;  // QK products per 32-key block
   constexpr int MT = D / 32;  // PV products (value-feature blocks)
-  __shared__ __attribute__((aligned(16))) char kbuf[2][kBC * D];
-  __shared__ __attribute__((aligned(16))) char vbuf[2][D * kBC];
+  using L = TileLoads<D>;
+  __shared__ __attribute__((aligned(1024))) char kbuf0[kBC * D], kbuf1[kBC * D], kbuf2[kBC * D];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[D * kBC], vbuf1[D * kBC], vbuf2[D * kBC];
 
   // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so slot
   // i runs tile (i % 8) * per_xcd + i / 8 and each XCD works through a contiguous
@@ -222,58 +276,48 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hl = lane >> 5;
   const int N = p.N;
+  const int ldv = p.ldv;
   const int q_base = qt * kRows;
   const int q0 = q_base + 32 * wave;  // this wavefront's first query row
   const int my_q = q0 + l32;
 
   const uint8_t* kh = p.k + (size_t)bh * N * D;
-  const uint8_t* vth = p.vt + (size_t)bh * D * p.ldv;
-
-  // Q (B operand of S^T = K Q^T): features 64m + 32h .. +31 of row my_q.
-  i32x8 qreg[MQ];
-#pragma unroll
-  for (int m = 0; m < MQ; ++m) {
-    if (my_q < N) {
-      const uint8_t* qp = p.q + ((size_t)bh * N + my_q) * D + 64 * m + 32 * hl;
-      const u32x4 a = *(const u32x4*)qp, b = *(const u32x4*)(qp + 16);
-      qreg[m] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-    } else {
-      qreg[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
+  const uint8_t* vth = p.vt + (size_t)bh * D * ldv;
 
   const int n_kv = (N + kBC - 1) / kBC;
   const int nt = CAUSAL ? min(n_kv, (q_base + kRows + kBC - 1) / kBC) : n_kv;
+
+  uint32_t koff[L::KPW], voff[L::VPW];
+  load_offsets<D>(koff, voff, wave, lane, ldv);
+
+  // Q (B operand of S^T = K Q^T): features 64m + 32h .. +31 of row my_q. Loaded
+  // after the first tiles' loads are issued and waited for at once (a wait the
+  // compiler sees), so that its own wait insertion finds no load outstanding in
+  // the tile loop.
+  i32x8 qreg[MQ];
+  auto load_q = [&] {
+    const __amdgpu_buffer_rsrc_t qr = rsrc(p.q + (size_t)bh * N * D, (uint32_t)N * D);
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      const uint32_t off = (uint32_t)(my_q * D + 64 * m + 32 * hl);
+      const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
+      const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, off + 16, 0, 0));
+      qreg[m] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  };
 
   f32x16 oacc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x16{};
   float m_used = -INFINITY, thr = -INFINITY, l_sum = 0.f;
-  const float c = p.c, tau = p.tau;
+  const float c = p.c, tau = p.tau, psum_thr = p.psum_thr;
 
-  Stage<D> stg;
-  uint32_t koff[Stage<D>::KCH], voff[Stage<D>::VCH];
-#pragma unroll
-  for (int i = 0; i < Stage<D>::KCH; ++i) {
-    const int id = tid + i * Stage<D>::NT;
-    koff[i] = (uint32_t)((id / (D / 16)) * D + 16 * (id % (D / 16)));
-  }
-  // V^T chunk id: feature id / 4, keys 16 * (id % 4) .. +15; id % 4 is the same for every i
-  const int vkey = 16 * (tid & 3);
-#pragma unroll
-  for (int i = 0; i < Stage<D>::VCH; ++i) {
-    const int id = tid + i * Stage<D>::NT;
-    voff[i] = (uint32_t)((id >> 2) * p.ldv + 16 * (id & 3));
-  }
-  stage_load<D>(stg, kh, vth, N, p.ldv, 0, koff, voff, vkey, kBC > N);
-  stage_store<D>(stg, kbuf[0], vbuf[0], tid);
-  __syncthreads();
-
-  // Products and softmax of tile t from the LDS tiles kb (K) and vb (V^T).
+  // Products and softmax of tile t from the LDS tiles kb (K, rows permuted) and vb (V^T).
   auto tile_step = [&](const char* kb, const char* vb, int t) __attribute__((always_inline)) {
     const int j0 = t * kBC;
 
-    // S^T = K Q^T for the two 32-key blocks
+    // S^T = K Q^T for the two 32-row blocks of the K tile
     f32x16 s[2];
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
@@ -283,91 +327,111 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
       for (int m = 0; m < MQ; ++m) s[cc] = mma(read32<D>(kb, r, 4 * m + 2 * hl, kswz<D>(r)), qreg[m], s[cc]);
     }
 
-    // mask keys past N and (causal) keys after the query, on boundary tiles only
+    // register r of block cc holds key j0 + 32 hl + 16 cc + r; mask keys past N and
+    // (causal) keys after the query, on boundary tiles only
     const bool masked = (j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > q0);
     if (masked) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * cc + 8 * (r / 4) + 4 * hl + (r % 4);
+          const int key = j0 + 32 * hl + 16 * cc + r;
           const bool hide = key >= N || (CAUSAL && key > my_q);
           s[cc][r] = hide ? -INFINITY : s[cc][r];
         }
     }
-    float red = s[0][0];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red = fmaxf(red, s[cc][r]);
-    const float m_tile = pair_max(red) * c;  // c > 0; -inf if every key of the row is masked
-    const bool need = m_tile > thr;
-    if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_used - m_tile) : 1.f;
-      m_used = need ? m_tile : m_used;
-      thr = m_used + tau;
-      l_sum *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[mt][r] *= alpha;
-    }
-    // P = 2^(s c - m_used), fp32 row sum, packed to e4m3: byte 16cc + r of the B operand
-    const float mc = -m_used;
-    i32x8 pb;
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        float e[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          e[b] = __builtin_amdgcn_exp2f(fmaf(s[cc][4 * a + b], c, mc));
-          l_sum += e[b];
-        }
-        int w = 0;
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], w, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
-        pb[4 * cc + a] = w;
-      }
 
-    // O^T += V^T P^T: value features 32mt + l32, this lane half's 32 keys
+    // P = 2^(s c - m) with the maximum in use and this lane's partial sum, packed to
+    // e4m3: byte 16 cc + r of the B operand is register r of block cc.
+    i32x8 pb;
+    auto exponentials = [&](float mc) -> float {
+      float part[2] = {0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float e[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            e[b] = __builtin_amdgcn_exp2f(fmaf(s[cc][4 * a + b], c, mc));
+            part[b & 1] += e[b];
+          }
+          int w = 0;
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], w, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
+          pb[4 * cc + a] = w;
+        }
+      return part[0] + part[1];
+    };
+    // The tile maximum is needed only when a rescale may be due: a row whose tile
+    // maximum exceeds m + tau has a P above 2^tau, so the partial sum of the lane
+    // holding that key exceeds 2^tau. The exponentials are taken with the maximum
+    // in use first; only a wavefront with such a sum (or with m still -inf, which
+    // gives +inf or NaN) computes the exact tile maximum, applies the threshold
+    // rule per row and takes the exponentials again.
+    float tsum = exponentials(-m_used);
+    if (__any(!(tsum <= psum_thr))) {
+      float red = s[0][0];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red = fmaxf(red, s[cc][r]);
+      const float m_tile = pair_max(red) * c;  // c > 0; -inf if every key of the row is masked
+      const bool need = m_tile > thr;
+      if (__any(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_used - m_tile) : 1.f;
+        m_used = need ? m_tile : m_used;
+        thr = m_used + tau;
+        l_sum *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[mt][r] *= alpha;
+        tsum = exponentials(-m_used);
+      }
+    }
+    l_sum += tsum;
+
+    // O^T += V^T P^T: value features 32 mt + l32, keys 32 hl .. 32 hl + 31
+    const bool tail = j0 + kBC > N;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int f = 32 * mt + l32;
-      oacc[mt] = mma(read32<kBC>(vb, f, 2 * hl, vswz(f)), pb, oacc[mt]);
+      i32x8 va = read32<kBC>(vb, f, 2 * hl, vswz(f));
+      if (tail) va = mask_tail(va, hl, N - j0);
+      oacc[mt] = mma(va, pb, oacc[mt]);
     }
   };
 
-  // One pipelined tile step; the loop below is unrolled by two so that each step's
-  // LDS buffer (BUF) is a compile-time constant and the LDS addresses fold into the
-  // instructions.
-  auto step = [&](auto buf_tag, int t) {
-    constexpr int BUF = decltype(buf_tag)::value;
-    const int j0 = t * kBC;
-    const bool more = t + 1 < nt;
-    if (more) stage_load<D>(stg, kh, vth, N, p.ldv, j0 + kBC, koff, voff, vkey, j0 + 2 * kBC > N);
-    tile_step(kbuf[BUF], vbuf[BUF], t);
-    if (more) stage_store<D>(stg, kbuf[BUF ^ 1], vbuf[BUF ^ 1], tid);
-    __syncthreads();
-  };
   if (REF) {
+    load_q();
     for (int t = 0; t < nt; ++t) {
-      if (t > 0) {
-        __syncthreads();
-        stage_load<D>(stg, kh, vth, N, p.ldv, t * kBC, koff, voff, vkey, (t + 1) * kBC > N);
-        stage_store<D>(stg, kbuf[0], vbuf[0], tid);
-        __syncthreads();
-      }
-      tile_step(kbuf[0], vbuf[0], t);
+      wait_barrier<0>();  // every wavefront is done reading the previous tile
+      load_tile<D>(koff, voff, kh, vth, N, ldv, t * kBC, true, kbuf0, vbuf0, wave);
+      wait_barrier<0>();  // this tile is in LDS for every wavefront
+      tile_step(kbuf0, vbuf0, t);
     }
   } else {
-    for (int t = 0; t < nt; t += 2) {
-      step(std::integral_constant<int, 0>{}, t);
-      if (t + 1 < nt) step(std::integral_constant<int, 1>{}, t + 1);
+    // Step t waits for tile t (this wavefront's loads of tile t+1 may still be in
+    // flight: PW of them), passes the barrier (every wavefront's loads of tile t
+    // landed and every wavefront finished step t-1, the last reader of the buffer
+    // tile t+2 goes to), issues tile t+2 and computes tile t. Tile t's buffer is
+    // buf[t % 3]; the loop is unrolled by three so the buffers are constants.
+    load_tile<D>(koff, voff, kh, vth, N, ldv, 0, true, kbuf0, vbuf0, wave);
+    load_tile<D>(koff, voff, kh, vth, N, ldv, kBC, nt > 1, kbuf1, vbuf1, wave);
+    load_q();  // waits for tiles 0 and 1 too: they were issued at the same time
+    auto step = [&](int t, const char* kb, const char* vb, char* kn, char* vn) __attribute__((always_inline)) {
+      wait_barrier<L::PW>();
+      load_tile<D>(koff, voff, kh, vth, N, ldv, (t + 2) * kBC, t + 2 < nt, kn, vn, wave);
+      tile_step(kb, vb, t);
+    };
+    for (int t = 0; t < nt; t += 3) {
+      step(t, kbuf0, vbuf0, kbuf2, vbuf2);
+      if (t + 1 < nt) step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
+      if (t + 2 < nt) step(t + 2, kbuf2, vbuf2, kbuf1, vbuf1);
     }
   }
-
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
 
   const float l_tot = pair_sum(l_sum);
   if (my_q < N) {

@@ -308,6 +308,57 @@ __device__ __forceinline__ void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Per-phase clock instrumentation, compiled in only with -DATTN_PHASE_CLOCKS (the
+// micro/phase_clocks.py tool builds such a library). Each wavefront sums, over its
+// tiles, the shader-clock cycles of its softmax phase, of the wait at the barrier
+// that ends it, of its matrix phase and of the wait at the barrier after that,
+// and stores the sums (with its tile count, total cycles and group) in place of
+// the rescale counts: 8 int32 per wavefront at (blockIdx.x * 8 + wave) * 8.
+struct PhaseClock {
+#ifdef ATTN_PHASE_CLOCKS
+  uint64_t acc[4] = {0, 0, 0, 0};
+  uint64_t prev = 0, begin = 0;
+  int tiles = 0;
+#endif
+  __device__ __forceinline__ void start() {
+#ifdef ATTN_PHASE_CLOCKS
+    begin = prev = __builtin_amdgcn_s_memtime();
+#endif
+  }
+  __device__ __forceinline__ void restart() {
+#ifdef ATTN_PHASE_CLOCKS
+    prev = __builtin_amdgcn_s_memtime();
+#endif
+  }
+  // The phase since the last mark ends here; f waits at the barrier that follows it.
+  template <int I, class F>
+  __device__ __forceinline__ void phase_then(F&& f) {
+#ifdef ATTN_PHASE_CLOCKS
+    const uint64_t a = __builtin_amdgcn_s_memtime();
+    f();
+    const uint64_t b = __builtin_amdgcn_s_memtime();
+    acc[I] += a - prev;
+    acc[I + 1] += b - a;
+    prev = b;
+    tiles += I == 2;
+#else
+    f();
+#endif
+  }
+  __device__ __forceinline__ void store(int* out, int slot, int wave, int lane, int grp) {
+#ifdef ATTN_PHASE_CLOCKS
+    if (out && lane == 0) {
+      int* o = out + (slot * 8 + wave) * 8;
+      for (int i = 0; i < 4; ++i) o[i] = (int)acc[i];
+      o[4] = tiles;
+      o[5] = (int)(__builtin_amdgcn_s_memtime() - begin);
+      o[6] = grp;
+      o[7] = 0;
+    }
+#endif
+  }
+};
+
 // VALU phase: mask (boundary tiles), adaptive rescale, P = 2^(s*c - m) with the
 // fp32 row sum, packed to bf16 in the PV operand order. The phase issues no LDS
 // reads: an LDS read holds its own wavefront's issue for about (bytes / 64)
@@ -688,6 +739,8 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   int slot = blockIdx.x;
   Tile tile;
   if (!find_tile(slot, tile)) return;
+  PhaseClock clk;
+  clk.start();
   issue_loads(tile);
   for (;;) {
   const int bh = tile.bh;
@@ -748,6 +801,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
       va[g][mt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, s, koffs);
+  clk.restart();
 
   // Every wavefront runs all n_tiles tiles of its workgroup: a tile past a causal
   // row's last visible key is fully masked (P = 0) and leaves m, l and O as they
@@ -771,14 +825,16 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     auto pair = [&](int k, char* kb0, char* kb1, char* vh0, char* vh1, char* vt0, char* vt1) {
       bf16x8 pb[NC][2];
       softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau);
-      wait_loads();
-      phase_barrier();
+      clk.phase_then<0>([&] {
+        wait_loads();
+        phase_barrier();
+      });
       matrix_phase<D, BC, NLD>(st, s, pb, va, qreg, kb1, vt0, vh1, voffs, koffs, lane, [&] {
         load_tile<D, BC, 4>(koff, kh, Nkv, (k + 2) * BC, kb0, wave & 3, k + 2 < n_tiles);
         load_tile<D, VHR, 4>(vhoff, vh, Nkv, (k + 2) * BC, vh0, wave & 3, k + 2 < n_tiles);
         load_tile<D, VTR, 4>(vtoff, vh, Nkv, (k + 1) * BC + VHR, vt1, wave & 3, k + 1 < n_tiles);
       });
-      phase_barrier();
+      clk.phase_then<2>(phase_barrier);
     };
     int k = 0;
     for (; k + 1 < n_tiles; k += 2) {
@@ -794,9 +850,9 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     auto pair = [&](int k, char* kb1, char* vh1, char* vt0) {
       bf16x8 pb[NC][2];
       softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau);
-      phase_barrier();
+      clk.phase_then<0>(phase_barrier);
       matrix_phase<D, BC, 0>(st, s, pb, va, qreg, kb1, vt0, vh1, voffs, koffs, lane, [] {});
-      phase_barrier();
+      clk.phase_then<2>(phase_barrier);
     };
     int k = 0;
     for (; k + 1 < n_tiles; k += 2) {
@@ -842,7 +898,9 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
       }
     if (hl == 0) {
       lse_out[row] = 0.69314718055994531f * (st.m_used + log2f(l_tot));
+#ifndef ATTN_PHASE_CLOCKS
       if (!SPLIT && p.rescale_count) p.rescale_count[row] = st.n_rescale;
+#endif
     }
   }
   if (!more) break;
@@ -850,6 +908,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   slot = next_slot;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
+  clk.store(SPLIT ? nullptr : p.rescale_count, blockIdx.x, wave, lane, grp);
 }
 
 // Merge of split-key partial results: for query row i of a head, the units

@@ -1,0 +1,76 @@
+"""Per-phase shader clocks of the bf16 forward kernel's ping-pong schedule.
+
+    python -m exact_attention_22_amd.micro.phase_clocks build      # on any host with hipcc
+    python -m exact_attention_22_amd.micro.phase_clocks run headline causal2k ...   # on the GPU
+
+`build` compiles the library with -DATTN_PHASE_CLOCKS into
+_build/libattn_fwd_phase.so. In that build every wavefront of the forward kernel
+sums the shader-clock cycles (s_memtime) of its softmax phases, of its waits at the
+barriers that end them, of its matrix phases and of the waits after those, and
+stores the sums in the rescale-count buffer instead of the counts. `run` loads that
+library (the EXACT_ATTN_LIB variable, set for a child process), runs each named
+workload three times and prints, for each group of wavefronts, the cycles per tile
+of the four intervals, and the total cycles per wavefront. The instrumentation
+adds four clock reads per tile and eight one-lane stores per wavefront at the end; the
+phases it times are otherwise the product kernel's.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+LIB = os.path.join(ROOT, "_build", "libattn_fwd_phase.so")
+
+
+def build() -> str:
+    from exact_attention_22_amd import build as lib_build
+    os.makedirs(os.path.dirname(LIB), exist_ok=True)
+    return lib_build.build(LIB, extra=["-DATTN_PHASE_CLOCKS"])
+
+
+def measure(names):
+    import torch
+
+    from exact_attention_22_amd import binding, inputs
+    assert os.path.samefile(binding.LIB_PATH, LIB), binding.LIB_PATH
+    dev = torch.device("cuda:0")
+    for name in names:
+        w = inputs.BY_NAME[name]
+        if isinstance(w, inputs.VarlenWorkload):
+            raise SystemExit(f"{name}: dense workloads only")
+        q, k, v = (t.to(dev) for t in inputs.workload_inputs(w))
+        for _ in range(3):
+            o, lse, rec = binding.attention(q, k, v, causal=w.causal, scale=w.scale, rescale_count=True)
+        torch.cuda.synchronize()
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        n = min(rec.numel() // 8, cus * 8)  # one record per wavefront of at most one workgroup per CU
+        r = rec.flatten()[: n * 8].view(-1, 8).cpu().double()
+        r = r[r[:, 4] > 0]
+        for g in (0, 1):
+            sel = r[r[:, 6] == g]
+            t = sel[:, 4].sum()
+            print(f"{name} group {'AB'[g]}: {len(sel)} wavefronts, {int(t)} tiles; cycles per tile: softmax "
+                  f"{sel[:, 0].sum() / t:.0f}, barrier wait {sel[:, 1].sum() / t:.0f}, matrix {sel[:, 2].sum() / t:.0f}, "
+                  f"barrier wait {sel[:, 3].sum() / t:.0f}; cycles per wavefront {sel[:, 5].mean():.0f} "
+                  f"({(sel[:, :4].sum(1)).mean():.0f} in tile steps)", flush=True)
+
+
+def main(argv):
+    if not argv or argv[0] not in ("build", "run"):
+        raise SystemExit(__doc__)
+    if argv[0] == "build":
+        print(build())
+        return 0
+    names = argv[1:] or ["headline"]
+    if os.environ.get("EXACT_ATTN_LIB") != LIB:
+        env = dict(os.environ, EXACT_ATTN_LIB=LIB)
+        return subprocess.run([sys.executable, "-m", "exact_attention_22_amd.micro.phase_clocks", "run", *names],
+                              cwd=ROOT, env=env).returncode
+    measure(names)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
