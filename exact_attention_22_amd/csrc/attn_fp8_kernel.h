@@ -65,7 +65,14 @@
 
 #include <type_traits>
 
+#include "lds_dma.h"
+
 namespace attn_fp8 {
+
+using attn_dma::dma16;
+using attn_dma::i32x4;
+using attn_dma::rsrc_words;
+using attn_dma::wait_barrier;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -174,32 +181,6 @@ __device__ __forceinline__ void load_offsets(uint32_t* koff, uint32_t* voff, int
   }
 }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor words for `bytes` bytes at `base`, as __builtin_amdgcn_make_buffer_rsrc
-// builds them (stride 0; third word the record count; fourth word DATA_FORMAT = 32-bit).
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFF), (int)bytes, 0x00020000};
-}
-
-// One direct-to-LDS load: 16 bytes per lane from byte offset voff of the buffer,
-// lane l's bytes at LDS byte 16 l of the 1 KiB run at `lds`. Inline asm, because the
-// compiler's wait insertion cannot tell the three K (or V^T) buffers apart once
-// they are one LDS block and would make every LDS read wait for the loads in
-// flight into the other two buffers, which undoes the second tile of lookahead.
-// The kernel places every wait on these loads itself (wait_barrier); the asm has
-// no register outputs, and its address operands are read when it issues.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is clobbered on purpose: the kernel keeps nothing in it
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, const char* lds) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(base), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
 // Issue the loads of the tile at key j0 (live: the tile exists) into kb and vb.
 // K reads through a resource that ends at row N, so keys past N load as zeros;
 // V^T through one that ends at the head's end (the last tile's columns past N
@@ -219,18 +200,6 @@ __device__ __forceinline__ void load_tile(const uint32_t* koff, const uint32_t* 
   for (int i = 0; i < L::KPW; ++i) dma16(kr, koff[i], kb + 1024 * (i * L::NW + wave));
 #pragma unroll
   for (int i = 0; i < L::VPW; ++i) dma16(vr, voff[i], vb + 1024 * (i * L::NW + wave));
-}
-
-// Wait until at most n of this wavefront's vector-memory loads are outstanding
-// (and its LDS reads are done), then the workgroup barrier. Loads complete in
-// issue order, so n = the loads issued after the ones needed.
-template <int N_OUT>
-__device__ __forceinline__ void wait_barrier() {
-  static_assert(N_OUT >= 0 && N_OUT < 16, "vmcnt field");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0070 | N_OUT);  // vmcnt(N_OUT), expcnt any, lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // 32 bytes of row `r` starting at logical chunk `ch` (two swizzled 16-byte chunks).
