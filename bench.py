@@ -45,8 +45,8 @@ KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip", "attn_fwd_launch.h", "att
 # counter reads for a 256 MiB device copy (FETCH x2.0, WRITE x1.0); see
 # profiles/attn_fwd_headline_counters.md. Valid only for the kernel sources
 # with this SHA-256; any change to them reports traffic as null.
-TRAFFIC = {"sources_sha256": "a745d2ddf32eff7c6976992f4b63f0662300c9c3acc2647960a12b9e3d3652e4",
-           "fetch_kib": 214350.0, "write_kib": 140800.0, "fetch_scale": 2.0, "write_scale": 1.0}
+TRAFFIC = {"sources_sha256": "5ea8bb44ea3522f9da5a48e833234caa591f67886af5c7af6006248a1b4af5cd",
+           "fetch_kib": 196777.0, "write_kib": 133120.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def kernel_sources_sha256() -> str:
@@ -85,6 +85,8 @@ def parse():
     ap.add_argument("--mode", choices=("forward", "backward", "splitkv", "fp8"), default="forward",
                     help="backward / splitkv: time only that path on --workload (a dense workload) and print "
                          "one short JSON line (for profiling); forward: the benchmark line")
+    ap.add_argument("--exp2-poly-eighths", type=int, default=0, choices=(0, 4, 8),
+                    help="forward timing with this many of every 8 exponentials on the polynomial (default 0)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (calibrates profiler byte counters)")
     return ap.parse_args()
@@ -414,7 +416,7 @@ def main():
         return
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = time_workload(w, args.steps, args.warmup)
+    ms = time_workload(w, args.steps, args.warmup, poly_eighths=args.exp2_poly_eighths)
     wall = time.perf_counter() - t0
     tflops = w.flops / (ms * 1e-3) / 1e12
     samples = None
@@ -492,11 +494,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {describe(w)} causal={w.causal} bf16 N(0,1) seed {w.seed}",
                    "B": w.B, "H": w.H, "Hkv": w.Hkv if is_varlen else w.kv_heads,
-                   "N": max(w.lengths) if is_varlen else w.N, "d": w.d, "causal": w.causal},
+                   "N": max(w.lengths) if is_varlen else w.N, "d": w.d, "causal": w.causal,
+                   "exp2_poly_eighths": args.exp2_poly_eighths},
         "frac_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_bytes(w.name)},
+                     "traffic": traffic_bytes(w.name) if args.exp2_poly_eighths == 0 else None},
         "timed_wall_s": round(wall, 2),
         "samples": samples,
         "workloads": others,

@@ -48,6 +48,14 @@ def measure(names):
         n = min(rec.numel() // 8, cus * 8)  # one record per wavefront of at most one workgroup per CU
         r = rec.flatten()[: n * 8].view(-1, 8).cpu().double()
         r = r[r[:, 4] > 0]
+        slots = rec.flatten()[: n * 8].view(-1, 8, 8).cpu().double()  # [workgroup][wavefront][record]
+        live = slots[:, :, 4].sum(1) > 0
+        wg = slots[:, :, 5].max(1).values[live]  # a workgroup's cycles: its slowest wavefront
+        ids = torch.arange(slots.shape[0])[live]
+        xcd = [wg[ids % 8 == x].mean().item() for x in range(8)]
+        print(f"{name} workgroups: {len(wg)}; cycles per workgroup min {wg.min():.0f}, median {wg.median():.0f}, "
+              f"max {wg.max():.0f}, mean {wg.mean():.0f} (max / mean {wg.max() / wg.mean():.3f}); mean per XCD "
+              f"{', '.join(f'{v:.0f}' for v in xcd)}", flush=True)
         for g in (0, 1):
             sel = r[r[:, 6] == g]
             t = sel[:, 4].sum()
