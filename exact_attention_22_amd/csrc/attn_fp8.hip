@@ -58,7 +58,7 @@ hipError_t launch(const attn_fp8::Fp8Params& p, bool ref, hipStream_t stream) {
   void* args[] = {const_cast<attn_fp8::Fp8Params*>(&p)};
   const void* fn = ref ? reinterpret_cast<const void*>(&attn_fp8::attn_fwd_fp8_kernel<D, CAUSAL, true>)
                        : reinterpret_cast<const void*>(&attn_fp8::attn_fwd_fp8_kernel<D, CAUSAL, false>);
-  return hipLaunchKernel(fn, dim3(8 * p.per_xcd), dim3(64 * attn_fp8::Shape<D>::NW), args, 0, stream);
+  return hipLaunchKernel(fn, dim3(p.n_xcd * p.per_xcd), dim3(64 * attn_fp8::Shape<D>::NW), args, 0, stream);
 }
 
 }  // namespace
@@ -93,7 +93,8 @@ attn_status_t attn_fwd_fp8_ex(const void* q, const void* k, const void* vt, void
   const int rows = d == 128 ? attn_fp8::Shape<128>::ROWS : attn_fp8::Shape<64>::ROWS;
   p.nq_tiles = (N + rows - 1) / rows;
   p.total_tiles = B * H * p.nq_tiles;
-  p.per_xcd = (p.total_tiles + 7) / 8;
+  p.n_xcd = attn_host::device_shape().xcds;
+  p.per_xcd = (p.total_tiles + p.n_xcd - 1) / p.n_xcd;
   p.c = scale * q_scale * k_scale * 1.44269504088896341f;
   p.ov = v_scale;
   p.tau = tau;

@@ -100,7 +100,8 @@ struct Fp8Params {
   int ldv;
   int nq_tiles;       // ceil(N / Shape<D>::ROWS)
   int total_tiles;    // B * H * nq_tiles
-  int per_xcd;        // ceil(total_tiles / 8)
+  int n_xcd;          // XCDs of the device (workgroup slot i runs on XCD i % n_xcd)
+  int per_xcd;        // ceil(total_tiles / n_xcd)
   float c;            // scale * q_scale * k_scale * log2(e) (> 0)
   float ov;           // v_scale
   float tau;          // rescale threshold, log2 units, in [0, 8]
@@ -231,11 +232,11 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
   __shared__ __attribute__((aligned(1024))) char kbuf0[kBC * D], kbuf1[kBC * D], kbuf2[kBC * D];
   __shared__ __attribute__((aligned(1024))) char vbuf0[D * kBC], vbuf1[D * kBC], vbuf2[D * kBC];
 
-  // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so slot
-  // i runs tile (i % 8) * per_xcd + i / 8 and each XCD works through a contiguous
+  // XCD-aware tile order: workgroups are dealt round-robin to the X XCDs, so slot
+  // i runs tile (i % X) * per_xcd + i / X and each XCD works through a contiguous
   // range (the query tiles of a head share that XCD's L2 for their K/V reads).
   const int slot = blockIdx.x;
-  const int tile = (slot & 7) * p.per_xcd + (slot >> 3);
+  const int tile = (slot % p.n_xcd) * p.per_xcd + slot / p.n_xcd;
   if (tile >= p.total_tiles) return;
   const int bh = tile / p.nq_tiles;
   int qt = tile % p.nq_tiles;

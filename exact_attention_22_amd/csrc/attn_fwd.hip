@@ -42,20 +42,34 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace attn_host
 
+namespace attn_host {
+
+DeviceShape device_shape() {
+  static std::atomic<int> cache[64];  // per device: xcds << 16 | cus, 0 = not yet read
+  const DeviceShape fallback{8, 256};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fallback;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0, xcds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1 ||
+        cus > 0xFFFF)
+      return fallback;
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1 || xcds > cus)
+      xcds = cus % 8 == 0 ? 8 : 1;
+    v = xcds << 16 | cus;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return DeviceShape{v >> 16, v & 0xFFFF};
+}
+
+}  // namespace attn_host
+
 namespace attn_launch {
 
 int cus_per_xcd() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) return 0;
-    v = cus / 8;
-    cache[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
+  const attn_host::DeviceShape ds = attn_host::device_shape();
+  return ds.cus / ds.xcds;
 }
 
 }  // namespace attn_launch
@@ -189,7 +203,8 @@ attn_status_t run(const Problem& P, int causal, const attn_fwd_opts* opts, void*
   const int seq = P.varlen ? (P.max_seqlen < P.N ? P.max_seqlen : P.N) : P.N;
   p.nq_tiles = (seq + kRows - 1) / kRows;
   p.total_tiles = P.B * P.H * p.nq_tiles;
-  p.per_xcd = (p.total_tiles + 7) / 8;
+  p.n_xcd = attn_host::device_shape().xcds;
+  p.per_xcd = (p.total_tiles + p.n_xcd - 1) / p.n_xcd;
   // c = scale * log2(e) in fp32. Masked scores are set to -inf (+inf for a negative
   // scale) and rely on s*c - m = -inf; for scale == 0 that product would be NaN, so
   // 0 is replaced by 2^-100. For inputs with |q|, |k| < 2^33 (at d <= 128,
@@ -223,7 +238,7 @@ void split_shape(int B, int H, int N, int d, int n_splits, int* splits, int* spl
   int s = n_splits;
   if (s <= 0) {
     const int64_t units = (int64_t)B * H * ((N + kRows - 1) / kRows);
-    const int cus = attn_launch::cus_per_xcd() > 0 ? attn_launch::cus_per_xcd() * 8 : 256;
+    const int cus = attn_host::device_shape().cus;
     s = units >= cus ? 1 : (int)((cus + units - 1) / units);
   }
   s = s < 1 ? 1 : (s > key_tiles ? key_tiles : s);
@@ -280,7 +295,8 @@ attn_status_t run_split(const Problem& P, int causal, int n_splits, void* ws, si
   p.G = P.H / P.Hkv;
   p.nq_tiles = (P.N + kRows - 1) / kRows;
   p.total_tiles = (int)units;
-  p.per_xcd = (p.total_tiles + 7) / 8;
+  p.n_xcd = attn_host::device_shape().xcds;
+  p.per_xcd = (p.total_tiles + p.n_xcd - 1) / p.n_xcd;
   p.c = P.scale * 1.44269504088896341f;
   if (p.c == 0.f) p.c = 0x1p-100f;
   p.tau = o2.rescale_tau_log2;

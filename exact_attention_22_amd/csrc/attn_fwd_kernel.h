@@ -92,7 +92,8 @@ struct Params {
   int G;               // query heads per key/value head (H / Hkv; 1 = multi-head)
   int nq_tiles;        // ceil(N / BR); packed batches: ceil(longest sequence / BR)
   int total_tiles;     // B * H * nq_tiles; packed batches: H * nseq * nq_tiles
-  int per_xcd;         // ceil(total_tiles / 8): workgroups per XCD slice
+  int n_xcd;           // XCDs of the device (workgroup slot v runs on XCD v % n_xcd)
+  int per_xcd;         // ceil(total_tiles / n_xcd): tiles per XCD slice
   float c;             // scale * log2(e) in fp32; +-2^-100 stands in for 0 (see the launcher)
   float tau;           // rescale threshold, log2 units
   float psum_thr;      // 2^tau * (1 - 2^-10): partial tile sums above it take the exact-maximum path
@@ -631,12 +632,12 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   const float tau = p.tau;
 
   // Tile v of the launch's virtual sequence: workgroup slot v runs logical tile
-  // (v % 8) * per_xcd + v / 8, so each XCD (slots are dealt round-robin to the 8
-  // XCDs) works through a contiguous range of tiles and the query tiles of one
-  // head share that XCD's L2. A launch with fewer workgroups than slots walks
-  // the slots v, v + gridDim.x, ... (gridDim.x is a multiple of 8, so a
-  // workgroup stays on its XCD's range); the next tile's Q, K_0, V_0 and K_1
-  // loads are then issued before the current tile's epilogue.
+  // (v % X) * per_xcd + v / X with X = n_xcd, so each XCD (slots are dealt
+  // round-robin to the X XCDs) works through a contiguous range of tiles and the
+  // query tiles of one head share that XCD's L2. A launch with fewer workgroups
+  // than slots walks the slots v, v + gridDim.x, ... (gridDim.x is a multiple of
+  // X, so a workgroup stays on its XCD's range); the next tile's Q, K_0, V_0 and
+  // K_1 loads are then issued before the current tile's epilogue.
   struct Tile {
     int bh, kvh, i0, n_tiles, t_full;  // kvh: the (batch, key/value head) that bh reads
     int n, start;  // packed batches: the sequence's length and first token (bh, kvh: heads)
@@ -648,18 +649,20 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   // pairs long tiles with short ones and every workgroup gets about the same
   // work, while the tiles running at the same time stay within few heads (their
   // K and V share the XCD's L2).
-  const int S = (int)gridDim.x >> 3;  // workgroups per XCD
+  const int X = p.n_xcd;
+  const int S = (int)gridDim.x / X;  // workgroups per XCD
   // Packed batches: logical tile (h * nseq + b) * nq_tiles + qt, so an XCD's range
-  // holds whole heads with all their sequences (equal work per XCD when 8 divides
+  // holds whole heads with all their sequences (equal work per XCD when X divides
   // H). Slots past a sequence's last query tile are empty (-1) and skipped.
   // Returns 1 for a tile, -1 for an empty slot, 0 past the end of the range.
   auto tile_of = [&](int v, Tile& t) -> int {
-    int j = v >> 3;
+    int j = v / X;
+    const int x = v - j * X;
     if (CAUSAL) {
       const int r = j / S, i = j - r * S;
       j = r * S + ((r & 1) ? S - 1 - i : i);
     }
-    const int logical = (v & 7) * p.per_xcd + j;
+    const int logical = x * p.per_xcd + j;
     if (j >= p.per_xcd || logical >= p.total_tiles) return 0;
     int unit = logical;
     if (SPLIT) {  // logical = (bh * nq_tiles + qt) * n_splits + sp

@@ -19,8 +19,7 @@ template <int D> struct Cfg;
 template <> struct Cfg<128> { static constexpr int BC = 64; };
 template <> struct Cfg<64> { static constexpr int BC = 64; };
 
-// Compute units per XCD of the current device (8 XCDs per MI355X), cached per
-// device; 0 if the runtime cannot tell (then every tile gets its own workgroup).
+// Workgroups per XCD of a persistent launch: one per compute unit of the XCD.
 int cus_per_xcd();
 
 // The forward kernel over dense or packed (varlen) rows: o_dtype fp32 or bf16, the

@@ -31,7 +31,7 @@ hipError_t launch(const attn::Params& p, bool neg, bool varlen, bool ref, hipStr
   int per_wg_xcd = p.per_xcd;
   const int slots = cus_per_xcd();
   if (slots > 0 && slots < per_wg_xcd) per_wg_xcd = slots;
-  const dim3 grid(per_wg_xcd * 8), block(64 * kWaves);
+  const dim3 grid(per_wg_xcd * p.n_xcd), block(64 * kWaves);
   void* args[] = {const_cast<attn::Params*>(&p)};
   const void* fn =
       neg ? kernel_fn<D, CAUSAL, OF32, POLY8, true>(varlen, ref) : kernel_fn<D, CAUSAL, OF32, POLY8, false>(varlen, ref);
@@ -63,7 +63,7 @@ hipError_t launch_split(const attn::Params& p, bool neg, bool of32, int rows_tot
       neg ? reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, true, 0, true, false, true>)
       : ref ? reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, true, 0, false, false, true, true>)
             : reinterpret_cast<const void*>(&attn::attn_fwd_kernel<D, Cfg<D>::BC, CAUSAL, true, 0, false, false, true>);
-  hipError_t e = hipLaunchKernel(fn, dim3(per_wg_xcd * 8), dim3(64 * kWaves), args, 0, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3(per_wg_xcd * p.n_xcd), dim3(64 * kWaves), args, 0, stream);
   if (e != hipSuccess) return e;
   int split_keys = p.split_tiles * Cfg<D>::BC;
   void* margs[] = {const_cast<attn::Params*>(&p), &rows_total, &split_keys};

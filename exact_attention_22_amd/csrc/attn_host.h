@@ -15,6 +15,16 @@ attn_status_t fail(attn_status_t s, const char* fmt, ...) __attribute__((format(
 // Whether the byte ranges [a, a+na) and [b, b+nb) intersect.
 bool overlaps(const void* a, size_t na, const void* b, size_t nb);
 
+// XCDs and compute units of the current device (cached per device). Workgroups are
+// dealt round-robin to the XCDs, so the kernels map workgroup slot v to XCD
+// v % xcds. {8, 256} (an MI355X) if the runtime cannot tell; any value is correct,
+// only the L2 locality of the tile order depends on it.
+struct DeviceShape {
+  int xcds;
+  int cus;
+};
+DeviceShape device_shape();
+
 }  // namespace attn_host
 
 #endif
