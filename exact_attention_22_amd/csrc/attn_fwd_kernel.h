@@ -360,55 +360,75 @@ struct PhaseClock {
   }
 };
 
-// VALU phase: mask (boundary tiles), adaptive rescale, P = 2^(s*c - m) with the
-// fp32 row sum, packed to bf16 in the PV operand order. The phase issues no LDS
-// reads: an LDS read holds its own wavefront's issue for about (bytes / 64)
-// cycles, which the matrix phase hides under its products and this phase cannot.
-template <int D, int BC, bool CAUSAL, int POLY8, bool NEG>
-__device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 32][2],
-                                              bool masked, int j0, int N, int my_q, int lane, float c, float tau) {
-  constexpr int NC = BC / 32;
-  constexpr int MT = D / 32;
+// Score halves U0 .. U1-1 of a tile (half u = 2 cc + h: registers 8h .. 8h+7 of
+// score block cc, one k-step of the PV product): mask keys >= N and (causal) keys
+// after the query (on boundary tiles), and P = 2^(s*c - m) with m the maximum in
+// use, packed to bf16 in the PV operand order; returns this lane's partial sum of
+// those halves. Two partial sums keep the additions off one dependency chain.
+template <int BC, bool CAUSAL, bool NEG, int U0, int U1>
+__device__ __forceinline__ void mask_blocks(f32x16 (&s)[BC / 32], bool masked, int j0, int N, int my_q, int lane) {
   constexpr float mask_val = NEG ? INFINITY : -INFINITY;
   const int hl = lane >> 5;
   if (masked) {
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
+    for (int u = U0; u < U1; ++u)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int j = 0; j < 8; ++j) {
+        const int cc = u / 2, r = 8 * (u % 2) + j;
         const int key = j0 + 32 * cc + 8 * (r / 4) + 4 * hl + (r % 4);
         const bool hide = key >= N || (CAUSAL && key > my_q);
         s[cc][r] = hide ? mask_val : s[cc][r];
       }
   }
-  // P = 2^(s*c - m) with the maximum in use m, and this lane's partial sum of the
-  // tile. Two partial sums keep the additions off one dependency chain.
-  auto exponentials = [&](float mc) -> float {
-    float part[2] = {0.f, 0.f};
+}
+template <int BC, int POLY8, int U0, int U1>
+__device__ __forceinline__ float exp_blocks(const f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 32][2], float c, float mc) {
+  float part[2] = {0.f, 0.f};
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
+  for (int u = U0; u < U1; ++u)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int j = 0; j < 8; ++j) {
+        const int cc = u / 2, h = u % 2, r = 8 * h + j;
+        const float x = fmaf(s[cc][r], c, mc);
+        float e;
+        if (POLY8 == 8 || (POLY8 == 4 && (r & 4)))
+          e = attn_exp2_poly(x);
+        else
+          e = __builtin_amdgcn_exp2f(x);
+        part[j & 1] += e;
+        pb[cc][h][j] = (__bf16)e;
+      }
+  // pack here: otherwise the packing sinks past the rescale check and keeps every
+  // fp32 exponential live until then
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * h + j;
-          const float x = fmaf(s[cc][r], c, mc);
-          float e;
-          if (POLY8 == 8 || (POLY8 == 4 && (r & 4)))
-            e = attn_exp2_poly(x);
-          else
-            e = __builtin_amdgcn_exp2f(x);
-          part[j & 1] += e;
-          pb[cc][h][j] = (__bf16)e;
-        }
-    // pack here: otherwise the packing sinks past the rescale check below and
-    // keeps every fp32 exponential live until then
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(pb[cc][h]));
-    return part[0] + part[1];
-  };
+  for (int u = U0; u < U1; ++u) asm volatile("" : "+v"(pb[u / 2][u % 2]));
+  return part[0] + part[1];
+}
+
+// At d = 64 the matrix phase (16 products) is much shorter than the softmax phase,
+// so the exponentials of a tile's first score half are taken at the end of the
+// matrix phase that computes the scores (PRE = 1 of the 2 NC halves), which
+// balances the two wavefronts of a SIMD; at d = 128 the softmax phase takes the
+// whole tile.
+template <int D>
+struct ExpSplit {
+  static constexpr int PRE = D == 64 ? 1 : 0;
+};
+
+// VALU phase: mask (boundary tiles), adaptive rescale, P = 2^(s*c - m) with the
+// fp32 row sum, packed to bf16 in the PV operand order. Score halves below PRE were
+// masked and exponentiated with the same maximum at the end of the previous
+// matrix phase; t_pre is their partial sum. The phase issues no LDS
+// reads: an LDS read holds its own wavefront's issue for about (bytes / 64)
+// cycles, which the matrix phase hides under its products and this phase cannot.
+template <int D, int BC, bool CAUSAL, int POLY8, bool NEG>
+__device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 32][2],
+                                              bool masked, int j0, int N, int my_q, int lane, float c, float tau,
+                                              float t_pre) {
+  constexpr int NC = BC / 32;
+  constexpr int MT = D / 32;
+  constexpr int PRE = ExpSplit<D>::PRE;
+  mask_blocks<BC, CAUSAL, NEG, PRE, 2 * NC>(s, masked, j0, N, my_q, lane);
   // The tile maximum is needed only when a rescale may be due: a row whose
   // tile maximum exceeds m + tau has a P above 2^tau, so the partial sum of the
   // lane holding that key exceeds 2^tau (the sum of non-negative terms is at
@@ -417,7 +437,8 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 
   // which gives +inf or NaN) computes the exact tile maximum, applies the
   // threshold rule per row and takes the exponentials again. The rescale policy
   // is unchanged; its maximum reduction leaves the common path.
-  float tsum = exponentials(-st.m_used);
+  float tsum = exp_blocks<BC, POLY8, PRE, 2 * NC>(s, pb, c, -st.m_used);
+  if (PRE > 0) tsum = t_pre + tsum;
   if (__any(!(tsum <= st.psum_thr))) {
     float red = s[0][0];
 #pragma unroll
@@ -437,7 +458,7 @@ __device__ __forceinline__ void softmax_phase(RowState<D>& st, f32x16 (&s)[BC / 
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.oacc[mt][r] *= alpha;
-      tsum = exponentials(-st.m_used);
+      tsum = exp_blocks<BC, POLY8, 0, 2 * NC>(s, pb, c, -st.m_used);
     }
   }
   st.l_sum += tsum;
@@ -500,12 +521,12 @@ __device__ __forceinline__ void pv_sched() {
 // one per product in the second half of the QK products. After a wavefront's
 // last tile the buffers hold stale data; that S and those operands are never
 // used.
-template <int D, int BC, int NLOADS, typename Loads>
+template <int D, int BC, int NLOADS, typename Loads, typename AfterQK>
 __device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 32], const bf16x8 (&pb)[BC / 32][2],
                                              bf16x8 (&va)[VSplit<D>::HKS][D / 32], const bf16x8 (&qreg)[D / 16],
                                              const char* kb, const char* vtl, const char* vhd_next,
                                              const int (&voffs)[D / 32], const int (&koffs)[D / 16], int lane,
-                                             Loads&& loads) {
+                                             Loads&& loads, AfterQK&& after_qk) {
   constexpr int NC = BC / 32;
   constexpr int MT = D / 32;
   constexpr int KK = D / 16;
@@ -556,6 +577,8 @@ __device__ __forceinline__ void matrix_phase(RowState<D>& st, f32x16 (&s)[BC / 3
   }
   __builtin_amdgcn_sched_group_barrier(0x008, KA, 0);
   __builtin_amdgcn_s_setprio(0);
+  // vector work on the new scores (the first block's exponentials at d = 64)
+  after_qk();
 }
 
 // O^T += V^T P^T of the reference schedule: the PV products of matrix_phase in
@@ -774,6 +797,17 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
 
   f32x16 s[NC];
   bf16x8 va[VSplit<D>::HKS][MT];  // PV operands of the head of the V tile the next matrix phase multiplies
+  bf16x8 pb[NC][2];                // P of the tile in flight, in the PV operand order
+  float t_pre = 0.f;               // partial row sum of its first ExpSplit<D>::PRE blocks
+  constexpr int PRE = ExpSplit<D>::PRE;
+  // the first PRE blocks of tile k's scores: masked and exponentiated right after the
+  // products that form them (the previous matrix phase, or the prologue)
+  auto pre_blocks = [&](int k) {
+    if (PRE > 0) {
+      mask_blocks<BC, CAUSAL, NEG, 0, PRE>(s, k >= t_full, (k + kt0) * BC, N, my_q, lane);
+      t_pre = exp_blocks<BC, POLY8, 0, PRE>(s, pb, c, -st.m_used);
+    }
+  };
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's tile and Q loads landed
   if (REF) {
     // reference schedule: one buffer per tensor, full waits, no phase offset
@@ -788,8 +822,9 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
       qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, s, koffs);
-      bf16x8 pb[NC][2];
-      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau);
+      pre_blocks(k);
+      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau,
+                                               t_pre);
       pv_reference<D, BC>(st, pb, vhd0, vtl0, voffs);
     }
     __syncthreads();
@@ -804,6 +839,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
       va[g][mt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   qk_part<D, NC, 0, NC * KK>(kbuf0, qreg, s, koffs);
+  pre_blocks(0);
   clk.restart();
 
   // Every wavefront runs all n_tiles tiles of its workgroup: a tile past a causal
@@ -826,8 +862,8 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
       LoadShape<D, BC, 4>::LPW + LoadShape<D, VHR, 4>::LPW + LoadShape<D, VTR, 4>::LPW;  // group A's loads per step
   if (grp == 0) {
     auto pair = [&](int k, char* kb0, char* kb1, char* vh0, char* vh1, char* vt0, char* vt1) {
-      bf16x8 pb[NC][2];
-      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau);
+      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau,
+                                               t_pre);
       clk.phase_then<0>([&] {
         wait_loads();
         phase_barrier();
@@ -836,7 +872,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
         load_tile<D, BC, 4>(koff, kh, Nkv, (k + 2) * BC, kb0, wave & 3, k + 2 < n_tiles);
         load_tile<D, VHR, 4>(vhoff, vh, Nkv, (k + 2) * BC, vh0, wave & 3, k + 2 < n_tiles);
         load_tile<D, VTR, 4>(vtoff, vh, Nkv, (k + 1) * BC + VHR, vt1, wave & 3, k + 1 < n_tiles);
-      });
+      }, [&] { pre_blocks(k + 1); });
       clk.phase_then<2>(phase_barrier);
     };
     int k = 0;
@@ -851,10 +887,11 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     phase_barrier();  // step 0: group B starts one phase behind
     // Steps 2k+1 (softmax(k)) and 2k+2 (matrix(k)).
     auto pair = [&](int k, char* kb1, char* vh1, char* vt0) {
-      bf16x8 pb[NC][2];
-      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau);
+      softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau,
+                                               t_pre);
       clk.phase_then<0>(phase_barrier);
-      matrix_phase<D, BC, 0>(st, s, pb, va, qreg, kb1, vt0, vh1, voffs, koffs, lane, [] {});
+      matrix_phase<D, BC, 0>(st, s, pb, va, qreg, kb1, vt0, vh1, voffs, koffs, lane, [] {},
+                             [&] { pre_blocks(k + 1); });
       clk.phase_then<2>(phase_barrier);
     };
     int k = 0;
