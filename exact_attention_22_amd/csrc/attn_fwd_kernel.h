@@ -284,16 +284,23 @@ struct RowState {
 // round-robin, so every SIMD holds one wavefront of each group and always has
 // one of them feeding the matrix core while the other runs the softmax.
 //
-// Global step 2k:   A: softmax(k)                 B: loads V_{k+1}; matrix(k-1)
-// Global step 2k+1: A: loads K_{k+2}; matrix(k)   B: softmax(k)
+// Global step 2k:   A: softmax(k)                 B: matrix(k-1)
+// Global step 2k+1: A: loads tiles; matrix(k)     B: softmax(k)
 // Each group runs pairs (softmax(k), matrix(k)), so the PV operands and P of a
-// tile live within one pair; group B starts with a step that only loads and
-// group A ends with an empty step, which keeps their barrier counts equal.
-// The softmax phase of tile t also reads V_t's PV operands from LDS, so V_t
-// must be resident one step before its product. Each group issues its tile
-// loads at the start of its matrix phase and waits for them at the end of its
-// next softmax phase, before the barrier; a tile issued at step s is therefore
-// visible from step s + 2, and its buffer was last read at step s - 1.
+// tile live within one pair; group B starts with an empty step and group A ends
+// with one. All LDS reads are issued in the matrix phases. Group A issues the
+// tile loads in its matrix phase and waits for them at the end of its next
+// softmax phase, before the barrier ending that step.
+//
+// Which steps end at a barrier depends on the head dim. Only the barriers after
+// even steps are needed for the LDS buffers (see the main loop); at d = 128 the
+// kernel has just those, and each wavefront's own order (A: matrix then
+// softmax, B: softmax then matrix) keeps the two groups of a SIMD in opposite
+// phases between them, give or take the difference of the phase lengths, while
+// no wavefront waits for the slowest SIMD halfway. At d = 64 the matrix phase
+// is much shorter than the softmax phase, and without a barrier after every
+// step the two softmax phases of a SIMD drift into each other; there every
+// step ends at a barrier.
 // ============================================================================
 
 // Barrier between phases. It waits for this wavefront's LDS reads and writes
@@ -845,8 +852,9 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   // Every wavefront runs all n_tiles tiles of its workgroup: a tile past a causal
   // row's last visible key is fully masked (P = 0) and leaves m, l and O as they
   // are, so no wavefront takes a separate code path. Tile k's buffers are
-  // kbuf[k % 2], vhd[k % 2] and vtl[k % 2]. Both groups pass 2 * n_tiles + 1
-  // barriers.
+  // kbuf[k % 2], vhd[k % 2] and vtl[k % 2]. Both groups pass n_tiles + 1
+  // barriers at d = 128 (those ending the even steps) and 2 * n_tiles + 1 at
+  // d = 64 (every step).
   //
   // LDS reads: matrix(k) (group A at step 2k+1, group B at step 2k+2) reads
   // V_k's tail, K_{k+1} and V_{k+1}'s head; the softmax phase reads none.
@@ -857,7 +865,23 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   // them at the end of softmax(k+1), before the barrier ending step 2k+2; all
   // three are first read at step 2k+3. Every barrier waits for the wavefront's
   // own LDS reads, so no buffer is overwritten under a read.
+  //
+  // The barriers ending the even steps suffice for this. Between the barrier
+  // ending step 2k and the one ending step 2k+2, the reads are those of
+  // matrix(k) in both groups (V_k's tail, K_{k+1}, V_{k+1}'s head), the writes
+  // those group A issues in matrix(k) (K_{k+2}, V_{k+2}'s head, V_{k+1}'s tail):
+  // different buffers. The buffers written were last read by matrix(k-1), which
+  // both groups finish before the barrier ending step 2k; the loads are waited
+  // for before the barrier ending step 2k+2, and first read after it.
+  constexpr bool EVERY_STEP = D == 64;  // also a barrier after the odd steps
   auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  // without a barrier: only keep the compiler from moving memory accesses across
+  auto odd_step_end = [] {
+    if (EVERY_STEP)
+      phase_barrier();
+    else
+      asm volatile("" ::: "memory");
+  };
   constexpr int NLD =
       LoadShape<D, BC, 4>::LPW + LoadShape<D, VHR, 4>::LPW + LoadShape<D, VTR, 4>::LPW;  // group A's loads per step
   if (grp == 0) {
@@ -873,7 +897,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
         load_tile<D, VHR, 4>(vhoff, vh, Nkv, (k + 2) * BC, vh0, wave & 3, k + 2 < n_tiles);
         load_tile<D, VTR, 4>(vtoff, vh, Nkv, (k + 1) * BC + VHR, vt1, wave & 3, k + 1 < n_tiles);
       }, [&] { pre_blocks(k + 1); });
-      clk.phase_then<2>(phase_barrier);
+      clk.phase_then<2>(odd_step_end);
     };
     int k = 0;
     for (; k + 1 < n_tiles; k += 2) {
@@ -889,7 +913,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
     auto pair = [&](int k, char* kb1, char* vh1, char* vt0) {
       softmax_phase<D, BC, CAUSAL, POLY8, NEG>(st, s, pb, k >= t_full, (k + kt0) * BC, N, my_q, lane, c, tau,
                                                t_pre);
-      clk.phase_then<0>(phase_barrier);
+      clk.phase_then<0>(odd_step_end);
       matrix_phase<D, BC, 0>(st, s, pb, va, qreg, kb1, vt0, vh1, voffs, koffs, lane, [] {},
                              [&] { pre_blocks(k + 1); });
       clk.phase_then<2>(phase_barrier);
