@@ -106,8 +106,13 @@ hipError_t launch(const attn_grad::BwdParams& p, int nb, int Hkv, hipStream_t st
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_grad::attn_bwd_dq_kernel<D, CAUSAL, VARLEN>),
                                  dim3(nb * p.H * p.n_tiles), block, args, 0, stream);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_grad::attn_bwd_dkdv_kernel<D, CAUSAL, VARLEN>),
-                         dim3(nb * Hkv * p.n_tiles), block, args, 0, stream);
+  // D = 128: wavefront pairs (two wavefronts per key block, eight per workgroup)
+  if constexpr (D == 128)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_grad::attn_bwd_dkdv_pair_kernel<D, CAUSAL, VARLEN>),
+                           dim3(nb * Hkv * p.n_tiles), dim3(2 * 64 * attn_grad::kWaves), args, 0, stream);
+  else
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_grad::attn_bwd_dkdv_kernel<D, CAUSAL, VARLEN>),
+                           dim3(nb * Hkv * p.n_tiles), block, args, 0, stream);
 }
 
 template <bool VARLEN>

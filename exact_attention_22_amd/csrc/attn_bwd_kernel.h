@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn_grad {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -423,6 +425,263 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(co
   if (my_k < N) {
     store_rows<D>(p.dk, kvrow0 + my_k, dka, p.scale, hl);
     store_rows<D>(p.dv, kvrow0 + my_k, dva, 1.f, hl);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dkdv kernel in wavefront pairs (used at D = 128): eight wavefronts, two per
+// SIMD, 128 key rows per workgroup. Wavefront w < 4 (the P wavefront) and
+// wavefront w + 4 (the dS wavefront) own the same 32 keys and run on the same
+// SIMD (wavefronts are dealt to the SIMDs round-robin). Per query tile:
+//   P wavefront:  S = Q K^T, P = exp2(S*c - LSE*log2 e) (masked), P to LDS in
+//                 fp32; barrier; dV^T += dO^T P.
+//   dS wavefront: dP = dO V^T; barrier; P from LDS, dS = P * (dP - D),
+//                 dK^T += Q^T dS.
+// Each holds one 128-feature accumulator and one operand row set (K or V), so
+// both fit 256 registers and the SIMD interleaves one wavefront's products with
+// the other's vector work. The arithmetic, and the order of every accumulation,
+// is that of attn_bwd_dkdv_kernel; P crosses LDS in fp32, so dK and dV are the
+// same bits. The P wavefronts issue the tile loads; the P buffer has one slot
+// per pair, written after the barrier that ends a step and read before the
+// next one. Wavefront 0 stores each LSE tile pre-multiplied by -log2(e) in LDS
+// once it has landed (the product the exponent needs per score).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's LDS accesses; loads in flight may stay
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Per-lane byte offsets of the A operands in a swizzled [64][D] LDS tile,
+// independent of the buffer and of the 32-row block (row reads) or 16-row group
+// (transpose reads): those add a constant that the read instruction carries.
+//   row[kk]:   row 32 cc + l % 32, chunk 2 kk + l / 32 (row_frag), + cc * 64 * D
+//   tr[mt][h]: the rows 16 j + 8 h + 4 (l / 32) + (l % 16) / 4 and columns
+//              32 mt + 16 ((l / 16) % 2) + 4 (l % 4) of tr4, + j * 32 * D
+template <int D>
+struct OperandOffsets {
+  int row[D / 16];
+  int tr[D / 32][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, hl = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) row[kk] = l32 * (2 * D) + (((2 * kk + hl) ^ swz<D>(l32)) << 4);
+    const int rl = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int cl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + rl, col = 32 * mt + cl;
+        tr[mt][h] = r * (2 * D) + (((col >> 3) ^ swz<D>(r)) << 4) + ((col & 7) << 1);
+      }
+  }
+  // From here on the compiler takes the offsets as changed: it adds the buffer's
+  // constant at each read instead of keeping one register per read and buffer.
+  __device__ __forceinline__ void launder() {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(row[kk]));
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) {
+      asm volatile("" : "+v"(tr[mt][0]));
+      asm volatile("" : "+v"(tr[mt][1]));
+    }
+  }
+};
+__device__ __forceinline__ bf16x8 row_at(const char* t, int off) { return *(const bf16x8*)(t + off); }
+__device__ __forceinline__ bf16x8 tr_at(const char* t, int off_lo, int off_hi) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_void*)(t + off_lo));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_void*)(t + off_hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int D, bool CAUSAL, bool VARLEN = false>
+__global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(const BwdParams p) {
+  constexpr int KK = D / 16, MT = D / 32, NC = kTile / 32;
+  constexpr int TB = kTile * D * 2;
+  __shared__ __attribute__((aligned(1024))) char qt0[TB];
+  __shared__ __attribute__((aligned(1024))) char qt1[TB];
+  __shared__ __attribute__((aligned(1024))) char dot0[TB];
+  __shared__ __attribute__((aligned(1024))) char dot1[TB];
+  __shared__ __attribute__((aligned(16))) float lse0[kTile];
+  __shared__ __attribute__((aligned(16))) float lse1[kTile];
+  __shared__ __attribute__((aligned(16))) float del0[kTile];
+  __shared__ __attribute__((aligned(16))) float del1[kTile];
+  // P of a pair's score block cc: registers 4g .. 4g+3 of lane l at [wave][cc][g][l]
+  __shared__ __attribute__((aligned(1024))) f32x4 pbuf[kWaves][NC][4][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = wv & 3;      // key block of the pair
+  const bool pw = wv < kWaves;  // P wavefront (K, dV) or dS wavefront (V, dK)
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int Hkv = p.H / p.G;
+  const int bg = blockIdx.x / p.n_tiles;  // dense: b * Hkv + g; packed: g * nseq + sequence
+  const int j0w = (blockIdx.x - bg * p.n_tiles) * kRows;
+  int N, g;
+  size_t kvrow0, qrow_first, qrow_step;  // query head hq starts at row qrow_first + hq * qrow_step
+  if (VARLEN) {
+    g = bg / p.nseq;
+    const int sq = bg - g * p.nseq;
+    int a, e;
+    seq_bounds(p, sq, a, e);
+    N = e - a;
+    if (j0w >= N) return;  // whole workgroup: past its sequence
+    kvrow0 = (size_t)g * p.N + a;
+    qrow_first = a;
+    qrow_step = p.N;
+  } else {
+    N = p.N;
+    const int b = bg / Hkv;
+    g = bg - b * Hkv;
+    kvrow0 = (size_t)bg * N;
+    qrow_first = (size_t)b * p.H * N;
+    qrow_step = N;
+  }
+  const size_t kvhead = kvrow0 * D;
+  const int my_k = j0w + 32 * wave + l32;
+
+  bf16x8 kvreg[KK];  // K rows (P wavefront) or V rows (dS wavefront) of the lane's key
+  load_row_operand<D>(kvreg, (pw ? p.k : p.v) + kvhead, N, my_k, hl);
+  f32x16 acc[MT];  // dV^T (P wavefront) or dK^T (dS wavefront)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+  OperandOffsets<D> oo;
+  oo.init(lane);
+  const int it0 = CAUSAL ? j0w / kTile : 0;
+  const int n_qt = (N + kTile - 1) / kTile;
+  const int per_head = n_qt - it0;
+  const int steps = per_head * p.G;
+  auto issue = [&](int st, char* Qb, char* dOb, float* lb, float* db) {
+    st = min(st, steps - 1);
+    const int hq = g * p.G + st / per_head;
+    const int iq0 = (it0 + st % per_head) * kTile;
+    const size_t qhead = qrow_first + (size_t)hq * qrow_step;
+    load_tile64<D>(p.q + qhead * D, N, iq0, Qb, wave, lane);
+    load_tile64<D>(p.dout + qhead * D, N, iq0, dOb, wave, lane);
+    if (wave == 0) load_vec64(p.lse + qhead, N, iq0, lb, lane);
+    if (wave == 1) load_vec64(p.delta + qhead, N, iq0, db, lane);
+  };
+  // wavefront 0 loaded the LSE tile: once it has landed, store -LSE * log2(e)
+  auto scale_lse = [&](float* lb) {
+    if (wv == 0) lb[lane] = -lb[lane] * 1.44269504088896341f;
+  };
+  if (pw) issue(0, qt0, dot0, lse0, del0);
+  __builtin_amdgcn_s_waitcnt(0);
+  scale_lse(lse0);
+  __syncthreads();
+  // P of score block cc (lane: key my_k, register r: query row 32 cc + 8 (r / 4) + 4 hl + r % 4)
+  // into the P buffer (fp32) and, as bf16, the B operands of dV
+  auto p_block = [&](auto masked, int cc, const f32x16& s, const float* nl, int iq0, bf16x8 (&pbc)[2]) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int qr = 32 * cc + 8 * gq + 4 * hl;
+      const f32x4 l4 = *(const f32x4*)&nl[qr];
+      f32x4 p4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * gq + e;
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, l4[e]));
+        if (decltype(masked)::value) {
+          const int qi = iq0 + qr + e;
+          pr = (qi >= N || (CAUSAL && my_k > qi)) ? 0.f : pr;
+        }
+        p4[e] = pr;
+        pbc[r / 8][r % 8] = (__bf16)pr;
+      }
+      pbuf[wave][cc][gq][lane] = p4;
+    }
+  };
+  // One loop per role (the role is uniform per wavefront), so that each keeps its
+  // accumulator in the same registers across the loop; both pass 2 barriers per step.
+  auto end_step = [&](float* lnx) {  // lnx: the next LSE tile (P wavefronts), else null
+    __builtin_amdgcn_s_waitcnt(0);     // the next tile's loads landed; this wavefront's LDS accesses done
+    if (lnx) scale_lse(lnx);
+    __syncthreads();
+  };
+  auto p_step = [&](int t, const char* Q, const char* dO, const float* lt, char* Qn, char* dOn, float* lnx,
+                    float* dn) {
+    oo.launder();
+    issue(t + 1, Qn, dOn, lnx, dn);
+    const int iq0 = (it0 + t % per_head) * kTile;
+    const bool edge = iq0 + kTile > N || (CAUSAL && iq0 < j0w + 32 * wave + 32);
+    bf16x8 pb[NC][2];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      f32x16 s;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_at(Q + cc * 64 * D, oo.row[kk]), kvreg[kk],
+                                                    kk == 0 ? f32x16{} : s, 0, 0, 0);
+      if (edge)
+        p_block(std::true_type{}, cc, s, lt, iq0, pb[cc]);
+      else
+        p_block(std::false_type{}, cc, s, lt, iq0, pb[cc]);
+    }
+    lds_barrier();  // P of this step in LDS
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_at(dO + (2 * cc + hh) * 32 * D, oo.tr[mt][0], oo.tr[mt][1]), pb[cc][hh], acc[mt], 0, 0, 0);
+    end_step(lnx);
+  };
+  auto ds_step = [&](const char* Q, const char* dO, const float* dt) {
+    oo.launder();
+    f32x16 dp[NC];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        dp[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_at(dO + cc * 64 * D, oo.row[kk]), kvreg[kk],
+                                                         kk == 0 ? f32x16{} : dp[cc], 0, 0, 0);
+    lds_barrier();  // P of this step in LDS
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int qr = 32 * cc + 8 * gq + 4 * hl;
+        const f32x4 d4 = *(const f32x4*)&dt[qr];
+        const f32x4 p4 = pbuf[wave][cc][gq][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * gq + e;
+          dsb[r / 8][r % 8] = (__bf16)(p4[e] * (dp[cc][r] - d4[e]));
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_at(Q + (2 * cc + hh) * 32 * D, oo.tr[mt][0], oo.tr[mt][1]), dsb[hh], acc[mt], 0, 0, 0);
+    }
+    end_step(nullptr);
+  };
+  if (pw) {
+    int t = 0;
+    for (; t + 1 < steps; t += 2) {
+      p_step(t, qt0, dot0, lse0, qt1, dot1, lse1, del1);
+      p_step(t + 1, qt1, dot1, lse1, qt0, dot0, lse0, del0);
+    }
+    if (t < steps) p_step(t, qt0, dot0, lse0, qt1, dot1, lse1, del1);
+  } else {
+    int t = 0;
+    for (; t + 1 < steps; t += 2) {
+      ds_step(qt0, dot0, del0);
+      ds_step(qt1, dot1, del1);
+    }
+    if (t < steps) ds_step(qt0, dot0, del0);
+  }
+  if (my_k < N) {
+    if (pw)
+      store_rows<D>(p.dv, kvrow0 + my_k, acc, 1.f, hl);
+    else
+      store_rows<D>(p.dk, kvrow0 + my_k, acc, p.scale, hl);
   }
 }
 
