@@ -42,7 +42,8 @@
 //
 // Layout: one workgroup = 4 wavefronts = 128 query rows of one (b, h), one
 // query row per lane (the S and O accumulators hold one query column per
-// lane), Q in registers; two workgroups share a compute unit at d = 128. K and
+// lane), Q in registers; three workgroups share a compute unit at d = 128 (at
+// most 168 registers per lane) and four at d = 64. K and
 // V^T tiles of 64 keys go from memory straight into LDS (buffer loads with the
 // LDS as destination, 16 bytes per lane), two tiles ahead of the products,
 // into three buffers: step t waits for tile t's loads (issued two steps
@@ -81,11 +82,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Wavefronts per workgroup (32 query rows each) for head dim D. Eight wavefronts
-// at D = 128 (one workgroup per compute unit instead of two) measured within 2 %.
+// at D = 128 (one workgroup per compute unit instead of two) measured within 2 % of
+// four on an earlier form of this kernel.
 template <int D>
 struct Shape {
   static constexpr int NW = 4;
   static constexpr int ROWS = 32 * NW;  // query rows per workgroup
+  static constexpr int PER_CU = D == 128 ? 3 : 4;  // workgroups per compute unit (registers, LDS)
 };
 constexpr int kMinRows = 128;  // smallest Shape<D>::ROWS
 constexpr int kBC = 64;        // keys per tile
@@ -197,10 +200,11 @@ __device__ __forceinline__ void load_tile(const uint32_t* koff, const uint32_t* 
   const uint32_t vrec = __builtin_amdgcn_readfirstlane(live ? (uint32_t)(D * ldv - j0) : 0u);
   const i32x4 kr = rsrc_words(kh + (size_t)(live ? j0 : 0) * D, krec);
   const i32x4 vr = rsrc_words(vth + (live ? j0 : 0), vrec);
+  const uint32_t kl = attn_dma::lds_addr(kb) + 1024u * wave, vl = attn_dma::lds_addr(vb) + 1024u * wave;
 #pragma unroll
-  for (int i = 0; i < L::KPW; ++i) dma16(kr, koff[i], kb + 1024 * (i * L::NW + wave));
+  for (int i = 0; i < L::KPW; ++i) dma16(kr, koff[i], kl + 1024u * i * L::NW);
 #pragma unroll
-  for (int i = 0; i < L::VPW; ++i) dma16(vr, voff[i], vb + 1024 * (i * L::NW + wave));
+  for (int i = 0; i < L::VPW; ++i) dma16(vr, voff[i], vl + 1024u * i * L::NW);
 }
 
 // 32 bytes of row `r` starting at logical chunk `ch` (two swizzled 16-byte chunks).
@@ -224,7 +228,7 @@ __device__ __forceinline__ i32x8 mask_tail(i32x8 a, int h, int valid) {
 }
 
 template <int D, bool CAUSAL, bool REF = false>
-__global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_fp8_kernel(const Fp8Params p) {
+__global__ void __launch_bounds__(64 * Shape<D>::NW, Shape<D>::PER_CU) attn_fwd_fp8_kernel(const Fp8Params p) {
   constexpr int kRows = Shape<D>::ROWS;
   constexpr int MQ = D / 64;  // QK products per 32-key block
   constexpr int MT = D / 32;  // PV products (value-feature blocks)
@@ -243,7 +247,8 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
   if (CAUSAL) qt = p.nq_tiles - 1 - qt;  // longest query tiles first
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // wave index in a scalar register: the tile loads' LDS destinations are then scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hl = lane >> 5;
   const int N = p.N;
   const int ldv = p.ldv;
@@ -280,6 +285,16 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
   f32x16 oacc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x16{};
+  // P of the current tile (B operand of the second product). Each 32-bit word is
+  // packed from four exponentials by two conversions that each write half of it;
+  // the first one keeps the other half of the word it is given, here the previous
+  // tile's P, which is dead by then (no separate zeroing per tile).
+  i32x8 pb = {};
+  // Per-lane byte offsets of a V^T operand in a tile buffer: row f = 32 mt + l32 at
+  // logical chunks 2 hl and 2 hl + 1 (the swizzle depends on f's bits 1..3 only, so
+  // value-feature block mt adds 32 mt rows, folded into the read instruction).
+  const int vo0 = l32 * kBC + (((2 * hl) ^ vswz(l32)) << 4);
+  const int vo1 = l32 * kBC + (((2 * hl + 1) ^ vswz(l32)) << 4);
   float m_used = -INFINITY, thr = -INFINITY, l_sum = 0.f;
   const float c = p.c, tau = p.tau, psum_thr = p.psum_thr;
 
@@ -313,7 +328,6 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
 
     // P = 2^(s c - m) with the maximum in use and this lane's partial sum, packed to
     // e4m3: byte 16 cc + r of the B operand is register r of block cc.
-    i32x8 pb;
     auto exponentials = [&](float mc) -> float {
       float part[2] = {0.f, 0.f};
 #pragma unroll
@@ -326,7 +340,7 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
             e[b] = __builtin_amdgcn_exp2f(fmaf(s[cc][4 * a + b], c, mc));
             part[b & 1] += e[b];
           }
-          int w = 0;
+          int w = pb[4 * cc + a];
           w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], w, false);
           w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
           pb[4 * cc + a] = w;
@@ -363,14 +377,19 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, 8 / Shape<D>::NW) attn_fwd_
     l_sum += tsum;
 
     // O^T += V^T P^T: value features 32 mt + l32, keys 32 hl .. 32 hl + 31
-    const bool tail = j0 + kBC > N;
+    i32x8 va[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int f = 32 * mt + l32;
-      i32x8 va = read32<kBC>(vb, f, 2 * hl, vswz(f));
-      if (tail) va = mask_tail(va, hl, N - j0);
-      oacc[mt] = mma(va, pb, oacc[mt]);
+      const u32x4 a = *(const u32x4*)(vb + vo0 + 32 * kBC * mt);
+      const u32x4 b = *(const u32x4*)(vb + vo1 + 32 * kBC * mt);
+      va[mt] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
     }
+    if (j0 + kBC > N) {  // last tile: keys past N
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) va[mt] = mask_tail(va[mt], hl, N - j0);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oacc[mt] = mma(va[mt], pb, oacc[mt]);
   };
 
   if (REF) {

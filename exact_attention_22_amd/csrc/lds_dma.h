@@ -37,6 +37,15 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, const char* lds
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(base), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
+// The same with the run's LDS byte address given as a (wave-uniform) integer.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
 // The same with 4 bytes per lane (lane l at LDS byte 4 l of the 256-byte run at `lds`).
 __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, const void* lds) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(
