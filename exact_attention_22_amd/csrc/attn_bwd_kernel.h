@@ -441,10 +441,12 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(co
 // both fit 256 registers and the SIMD interleaves one wavefront's products with
 // the other's vector work. The arithmetic, and the order of every accumulation,
 // is that of attn_bwd_dkdv_kernel; P crosses LDS in fp32, so dK and dV are the
-// same bits. The P wavefronts issue the tile loads; the P buffer has one slot
-// per pair, written after the barrier that ends a step and read before the
-// next one. Wavefront 0 stores each LSE tile pre-multiplied by -log2(e) in LDS
-// once it has landed (the product the exponent needs per score).
+// same bits. The dS wavefronts issue the next step's tile loads right after
+// their dP products (the P wavefront's exponentials make them wait there
+// anyway); the P buffer has one slot per pair, written after the barrier that
+// ends a step and read before the next one. Wavefront 4 (the first dS
+// wavefront) stores each LSE tile pre-multiplied by -log2(e) in LDS once it has
+// landed (the product the exponent needs per score).
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's LDS accesses; loads in flight may stay
@@ -562,11 +564,13 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(const BwdPar
     if (wave == 0) load_vec64(p.lse + qhead, N, iq0, lb, lane);
     if (wave == 1) load_vec64(p.delta + qhead, N, iq0, db, lane);
   };
-  // wavefront 0 loaded the LSE tile: once it has landed, store -LSE * log2(e)
+  // the dS wavefronts issue the tile loads (in the part of a step where they would
+  // otherwise wait for P); the first of them loads the LSE tile and, once it has
+  // landed, stores -LSE * log2(e)
   auto scale_lse = [&](float* lb) {
-    if (wv == 0) lb[lane] = -lb[lane] * 1.44269504088896341f;
+    if (wv == kWaves) lb[lane] = -lb[lane] * 1.44269504088896341f;
   };
-  if (pw) issue(0, qt0, dot0, lse0, del0);
+  if (!pw) issue(0, qt0, dot0, lse0, del0);
   __builtin_amdgcn_s_waitcnt(0);
   scale_lse(lse0);
   __syncthreads();
@@ -594,50 +598,85 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(const BwdPar
   };
   // One loop per role (the role is uniform per wavefront), so that each keeps its
   // accumulator in the same registers across the loop; both pass 2 barriers per step.
-  auto end_step = [&](float* lnx) {  // lnx: the next LSE tile (P wavefronts), else null
+  auto end_step = [&](float* lnx) {  // lnx: the next LSE tile (dS wavefronts), else null
     __builtin_amdgcn_s_waitcnt(0);     // the next tile's loads landed; this wavefront's LDS accesses done
     if (lnx) scale_lse(lnx);
     __syncthreads();
   };
-  auto p_step = [&](int t, const char* Q, const char* dO, const float* lt, char* Qn, char* dOn, float* lnx,
-                    float* dn) {
+  // The products' A operands come from LDS: row fragments (S, dP) and transpose
+  // reads (dV, dK). Each is read RA products ahead of its use, so a product never
+  // waits for the read that feeds it; the transpose reads of the second products
+  // start before the barrier between the two halves of a step (the tiles are
+  // resident from the step's first barrier on).
+  constexpr int NRF = NC * KK;      // row-fragment products per step (S or dP)
+  constexpr int NTR = NC * 2 * MT;  // transpose-operand products per step (dV or dK)
+  constexpr int RA = 4;
+  // row-fragment chain: x[cc] = sum_kk A(tile rows 32 cc.., chunk kk) . kvreg[kk]; `after(cc)`
+  // runs when block cc's chain has been issued
+  auto row_chain = [&](const char* T, f32x16 (&x)[NC], auto&& after) {
+    bf16x8 rf[NRF];
+    auto rd = [&](int f) { rf[f] = row_at(T + (f / KK) * 64 * D, oo.row[f % KK]); };
+#pragma unroll
+    for (int f = 0; f < RA; ++f) rd(f);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int f = cc * KK + kk;
+        if (f + RA < NRF) rd(f + RA);
+        x[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf[f], kvreg[kk], kk == 0 ? f32x16{} : x[cc], 0, 0, 0);
+      }
+      if (cc == 0) __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (cc * KK + kk + RA < NRF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      after(cc);
+    }
+  };
+  // transpose operand i = (2 cc + hh) * MT + mt of tile T
+  auto tr_read = [&](const char* T, int i) {
+    return tr_at(T + (i / MT) * 32 * D, oo.tr[i % MT][0], oo.tr[i % MT][1]);
+  };
+  auto p_step = [&](int t, const char* Q, const char* dO, const float* lt) {
     oo.launder();
-    issue(t + 1, Qn, dOn, lnx, dn);
     const int iq0 = (it0 + t % per_head) * kTile;
     const bool edge = iq0 + kTile > N || (CAUSAL && iq0 < j0w + 32 * wave + 32);
     bf16x8 pb[NC][2];
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      f32x16 s;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_at(Q + cc * 64 * D, oo.row[kk]), kvreg[kk],
-                                                    kk == 0 ? f32x16{} : s, 0, 0, 0);
+    f32x16 s[NC];
+    row_chain(Q, s, [&](int cc) {
       if (edge)
-        p_block(std::true_type{}, cc, s, lt, iq0, pb[cc]);
+        p_block(std::true_type{}, cc, s[cc], lt, iq0, pb[cc]);
       else
-        p_block(std::false_type{}, cc, s, lt, iq0, pb[cc]);
-    }
+        p_block(std::false_type{}, cc, s[cc], lt, iq0, pb[cc]);
+    });
+    bf16x8 vf[NTR];
+#pragma unroll
+    for (int i = 0; i < RA; ++i) vf[i] = tr_read(dO, i);
     lds_barrier();  // P of this step in LDS
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
+    for (int i = 0; i < NTR; ++i) {
+      if (i + RA < NTR) vf[i + RA] = tr_read(dO, i + RA);
+      const int cc = i / (2 * MT), hh = (i / MT) % 2, mt = i % MT;
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pb[cc][hh], acc[mt], 0, 0, 0);
+    }
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_at(dO + (2 * cc + hh) * 32 * D, oo.tr[mt][0], oo.tr[mt][1]), pb[cc][hh], acc[mt], 0, 0, 0);
-    end_step(lnx);
+    for (int i = 0; i < NTR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + RA < NTR) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    end_step(nullptr);
   };
-  auto ds_step = [&](const char* Q, const char* dO, const float* dt) {
+  auto ds_step = [&](int t, const char* Q, const char* dO, const float* dt, char* Qn, char* dOn, float* lnx,
+                     float* dn) {
     oo.launder();
     f32x16 dp[NC];
+    row_chain(dO, dp, [](int) {});
+    issue(t + 1, Qn, dOn, lnx, dn);
+    bf16x8 kf[NTR];
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        dp[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_at(dO + cc * 64 * D, oo.row[kk]), kvreg[kk],
-                                                         kk == 0 ? f32x16{} : dp[cc], 0, 0, 0);
+    for (int i = 0; i < RA; ++i) kf[i] = tr_read(Q, i);
     lds_barrier();  // P of this step in LDS
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
@@ -654,28 +693,29 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(const BwdPar
         }
       }
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_at(Q + (2 * cc + hh) * 32 * D, oo.tr[mt][0], oo.tr[mt][1]), dsb[hh], acc[mt], 0, 0, 0);
+      for (int j = 0; j < 2 * MT; ++j) {
+        const int i = cc * 2 * MT + j;
+        if (i + RA < NTR) kf[i + RA] = tr_read(Q, i + RA);
+        const int hh = j / MT, mt = j % MT;
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], dsb[hh], acc[mt], 0, 0, 0);
+      }
     }
-    end_step(nullptr);
+    end_step(lnx);
   };
   if (pw) {
     int t = 0;
     for (; t + 1 < steps; t += 2) {
-      p_step(t, qt0, dot0, lse0, qt1, dot1, lse1, del1);
-      p_step(t + 1, qt1, dot1, lse1, qt0, dot0, lse0, del0);
+      p_step(t, qt0, dot0, lse0);
+      p_step(t + 1, qt1, dot1, lse1);
     }
-    if (t < steps) p_step(t, qt0, dot0, lse0, qt1, dot1, lse1, del1);
+    if (t < steps) p_step(t, qt0, dot0, lse0);
   } else {
     int t = 0;
     for (; t + 1 < steps; t += 2) {
-      ds_step(qt0, dot0, del0);
-      ds_step(qt1, dot1, del1);
+      ds_step(t, qt0, dot0, del0, qt1, dot1, lse1, del1);
+      ds_step(t + 1, qt1, dot1, del1, qt0, dot0, lse0, del0);
     }
-    if (t < steps) ds_step(qt0, dot0, del0);
+    if (t < steps) ds_step(t, qt0, dot0, del0, qt1, dot1, lse1, del1);
   }
   if (my_k < N) {
     if (pw)
