@@ -183,6 +183,56 @@ __device__ __forceinline__ void seq_bounds(const BwdParams& p, int s, int& a, in
   e = min(max(p.cu_seqlens[s + 1], a), p.N);
 }
 
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's LDS accesses; loads in flight may stay
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Per-lane byte offsets of the A operands in a swizzled [64][D] LDS tile,
+// independent of the buffer and of the 32-row block (row reads) or 16-row group
+// (transpose reads): those add a constant that the read instruction carries.
+//   row[kk]:   row 32 cc + l % 32, chunk 2 kk + l / 32 (row_frag), + cc * 64 * D
+//   tr[mt][h]: the rows 16 j + 8 h + 4 (l / 32) + (l % 16) / 4 and columns
+//              32 mt + 16 ((l / 16) % 2) + 4 (l % 4) of tr4, + j * 32 * D
+template <int D>
+struct OperandOffsets {
+  int row[D / 16];
+  int tr[D / 32][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, hl = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) row[kk] = l32 * (2 * D) + (((2 * kk + hl) ^ swz<D>(l32)) << 4);
+    const int rl = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int cl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + rl, col = 32 * mt + cl;
+        tr[mt][h] = r * (2 * D) + (((col >> 3) ^ swz<D>(r)) << 4) + ((col & 7) << 1);
+      }
+  }
+  // From here on the compiler takes the offsets as changed: it adds the buffer's
+  // constant at each read instead of keeping one register per read and buffer.
+  __device__ __forceinline__ void launder() {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(row[kk]));
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) {
+      asm volatile("" : "+v"(tr[mt][0]));
+      asm volatile("" : "+v"(tr[mt][1]));
+    }
+  }
+};
+__device__ __forceinline__ bf16x8 row_at(const char* t, int off) { return *(const bf16x8*)(t + off); }
+__device__ __forceinline__ bf16x8 tr_at(const char* t, int off_lo, int off_hi) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_void*)(t + off_lo));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_void*)(t + off_hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // ---------------------------------------------------------------------------
 // dq kernel: workgroup = (b, h, 128 query rows); packed batches (VARLEN):
 // workgroup = (h, sequence, 128 query rows of that sequence).
@@ -247,23 +297,49 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) 
   load_tile64<D>(p.k + kvhead, N, 0, kt0, wave, lane);
   load_tile64<D>(p.v + kvhead, N, 0, vt0, wave, lane);
   sync_tiles();
+  OperandOffsets<D> oo;
+  oo.init(lane);
+  // The products' A operands are read ahead of their use: the K and V row fragments
+  // of S and dP RA k-steps ahead, the transpose operands of dQ RT products ahead
+  // (the first RT of a block before its dS).
+  constexpr int NRF = NC * KK, RA = 2, NTR = 2 * MT, RT = 2;
   // Step t computes on (K, V) while tile t+1 loads into (Kn, Vn); the loads are
   // unconditional (past the last tile they read beyond kv_end or, past N, nothing).
   auto step = [&](int t, const char* K, const char* V, char* Kn, char* Vn) {
+    oo.launder();
     const int j0 = t * kTile;
     load_tile64<D>(p.k + kvhead, N, j0 + kTile, Kn, wave, lane);
     load_tile64<D>(p.v + kvhead, N, j0 + kTile, Vn, wave, lane);
     const bool edge = j0 + kTile > N || (CAUSAL && j0 + kTile - 1 > i0 + 32 * wave);
+    bf16x8 kr[NRF], vr[NRF];
+    auto rd = [&](int f) {
+      kr[f] = row_at(K + (f / KK) * 64 * D, oo.row[f % KK]);
+      vr[f] = row_at(V + (f / KK) * 64 * D, oo.row[f % KK]);
+    };
+#pragma unroll
+    for (int f = 0; f < RA; ++f) rd(f);
     // One 32-key block at a time, so that only one block's scores are live.
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(K, 32 * cc + l32, 2 * kk + hl), qreg[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(V, 32 * cc + l32, 2 * kk + hl), doreg[kk], dp, 0, 0,
-                                                     0);
+        const int f = cc * KK + kk;
+        if (f + RA < NRF) rd(f + RA);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[f], qreg[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[f], doreg[kk], dp, 0, 0, 0);
       }
+      if (cc == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * RA, 0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (cc * KK + kk + RA < NRF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      // transpose operands of this block's dQ products, i = 2 * hh + ... (hh, mt)
+      bf16x8 tq[NTR];
+      auto trd = [&](int j) { tq[j] = tr_at(K + (2 * cc + j / MT) * 32 * D, oo.tr[j % MT][0], oo.tr[j % MT][1]); };
+#pragma unroll
+      for (int j = 0; j < RT; ++j) trd(j);
       // dS^T in the B-operand order of the next product: k-step 2*cc + hh holds keys
       // 32*cc + 16*hh + 8*(j/4) + 4*hl + j%4 (register r = 8*hh + j of the block).
       bf16x8 dsb[2];
@@ -277,11 +353,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) 
         dsb[r / 8][r % 8] = (__bf16)(pr * (dp[r] - Di));
       }
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(K, 32 * cc + 16 * hh, 32 * mt, lane),
-                                                            dsb[hh], acc[mt], 0, 0, 0);
+      for (int j = 0; j < NTR; ++j) {
+        if (j + RT < NTR) trd(j + RT);
+        acc[j % MT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[j], dsb[j / MT], acc[j % MT], 0, 0, 0);
+      }
     }
     sync_tiles();
   };
@@ -447,56 +522,6 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(co
 // ends a step and read before the next one. Wavefront 4 (the first dS
 // wavefront) stores each LSE tile pre-multiplied by -log2(e) in LDS once it has
 // landed (the product the exponent needs per score).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's LDS accesses; loads in flight may stay
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Per-lane byte offsets of the A operands in a swizzled [64][D] LDS tile,
-// independent of the buffer and of the 32-row block (row reads) or 16-row group
-// (transpose reads): those add a constant that the read instruction carries.
-//   row[kk]:   row 32 cc + l % 32, chunk 2 kk + l / 32 (row_frag), + cc * 64 * D
-//   tr[mt][h]: the rows 16 j + 8 h + 4 (l / 32) + (l % 16) / 4 and columns
-//              32 mt + 16 ((l / 16) % 2) + 4 (l % 4) of tr4, + j * 32 * D
-template <int D>
-struct OperandOffsets {
-  int row[D / 16];
-  int tr[D / 32][2];
-  __device__ __forceinline__ void init(int lane) {
-    const int l32 = lane & 31, hl = lane >> 5;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) row[kk] = l32 * (2 * D) + (((2 * kk + hl) ^ swz<D>(l32)) << 4);
-    const int rl = 4 * (lane >> 5) + ((lane & 15) >> 2);
-    const int cl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = 8 * h + rl, col = 32 * mt + cl;
-        tr[mt][h] = r * (2 * D) + (((col >> 3) ^ swz<D>(r)) << 4) + ((col & 7) << 1);
-      }
-  }
-  // From here on the compiler takes the offsets as changed: it adds the buffer's
-  // constant at each read instead of keeping one register per read and buffer.
-  __device__ __forceinline__ void launder() {
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(row[kk]));
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt) {
-      asm volatile("" : "+v"(tr[mt][0]));
-      asm volatile("" : "+v"(tr[mt][1]));
-    }
-  }
-};
-__device__ __forceinline__ bf16x8 row_at(const char* t, int off) { return *(const bf16x8*)(t + off); }
-__device__ __forceinline__ bf16x8 tr_at(const char* t, int off_lo, int off_hi) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_void*)(t + off_lo));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_void*)(t + off_hi));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 template <int D, bool CAUSAL, bool VARLEN = false>
 __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(const BwdParams p) {
   constexpr int KK = D / 16, MT = D / 32, NC = kTile / 32;
