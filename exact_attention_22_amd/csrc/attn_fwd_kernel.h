@@ -77,6 +77,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Params {
   const __bf16* q;
@@ -940,26 +941,53 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(const Params p) {
   // sees none of the unit's keys stores a value the merge does not read)
   float* const o_out = SPLIT ? p.ws_o + (size_t)tile.sp * p.split_stride * D : (float*)p.o;
   float* const lse_out = SPLIT ? p.ws_lse + (size_t)tile.sp * p.split_stride : p.lse;
-  if (my_q < N) {
-    const float inv = 1.f / l_tot;
-    const size_t row = row0 + my_q;
+  const float inv = 1.f / l_tot;
+  // bf16 output: lanes l and l ^ 32 hold the same row, lane half hl the features
+  // 32 mt + 8 gq + 4 hl + e (register 4 gq + e). One lane-half exchange per pair of
+  // gq gives each lane 8 consecutive features (gq = 2 pp + hl, 16 bytes), so a row
+  // takes 8 stores of 16 bytes per lane instead of 16 of 8 bytes. The exchange
+  // runs in every lane (a row past N only skips the stores).
+  u32x4 ob[OF32 ? 1 : MT][2];
+  if (!OF32) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int dv = 32 * mt + 8 * gq + 4 * hl;
-        if (OF32) {
+      for (int pp = 0; pp < 2; ++pp) {
+        bf16x4 a, b;  // gq = 2 pp (kept by hl = 0) and gq = 2 pp + 1 (kept by hl = 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = (__bf16)(st.oacc[mt][8 * pp + e] * inv);
+          b[e] = (__bf16)(st.oacc[mt][8 * pp + 4 + e] * inv);
+        }
+        u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          // x of the upper lane half <-> y of the lower lane half
+          const auto r = __builtin_amdgcn_permlane32_swap(x[j], y[j], false, false);
+          x[j] = r[0];
+          y[j] = r[1];
+        }
+        ob[OF32 ? 0 : mt][pp] = u32x4{x[0], x[1], y[0], y[1]};
+      }
+  }
+  if (my_q < N) {
+    const size_t row = row0 + my_q;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (OF32) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
           f32x4 w;
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[e] = st.oacc[mt][4 * gq + e] * inv;
-          *(f32x4*)(o_out + row * D + dv) = w;
-        } else {
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.oacc[mt][4 * gq + e] * inv);
-          *(bf16x4*)((__bf16*)p.o + row * D + dv) = w;
+          *(f32x4*)(o_out + row * D + 32 * mt + 8 * gq + 4 * hl) = w;
         }
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+          *(u32x4*)((__bf16*)p.o + row * D + 32 * mt + 16 * pp + 8 * hl) = ob[OF32 ? 0 : mt][pp];
       }
+    }
     if (hl == 0) {
       lse_out[row] = 0.69314718055994531f * (st.m_used + log2f(l_tot));
 #ifndef ATTN_PHASE_CLOCKS
