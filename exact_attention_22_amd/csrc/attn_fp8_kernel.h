@@ -423,18 +423,37 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, Shape<D>::PER_CU) attn_fwd_
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
 
   const float l_tot = pair_sum(l_sum);
+  // Lanes l and l ^ 32 hold the same row, lane half hl the features 32 mt + 8 gq +
+  // 4 hl + e (register 4 gq + e). One lane-half exchange per pair of gq gives each
+  // lane 8 consecutive features (gq = 2 pp + hl), stored as 16 bytes. The exchange
+  // runs in every lane (a row past N only skips the stores).
+  const float inv = p.ov / l_tot;
+  u32x4 ob[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      bf16x4 a, b;  // gq = 2 pp (kept by hl = 0) and gq = 2 pp + 1 (kept by hl = 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = (__bf16)(oacc[mt][8 * pp + e] * inv);
+        b[e] = (__bf16)(oacc[mt][8 * pp + 4 + e] * inv);
+      }
+      u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {  // x of the upper lane half <-> y of the lower lane half
+        const auto r = __builtin_amdgcn_permlane32_swap(x[j], y[j], false, false);
+        x[j] = r[0];
+        y[j] = r[1];
+      }
+      ob[mt][pp] = u32x4{x[0], x[1], y[0], y[1]};
+    }
   if (my_q < N) {
-    const float inv = p.ov / l_tot;
     const size_t row = (size_t)bh * N + my_q;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[mt][4 * gq + e] * inv);
-        *(bf16x4*)(p.o + row * D + 32 * mt + 8 * gq + 4 * hl) = w;
-      }
+      for (int pp = 0; pp < 2; ++pp) *(u32x4*)(p.o + row * D + 32 * mt + 16 * pp + 8 * hl) = ob[mt][pp];
     if (hl == 0) p.lse[row] = 0.69314718055994531f * (m_used + log2f(l_tot));
   }
 }
