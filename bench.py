@@ -45,8 +45,8 @@ KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip", "attn_fwd_launch.h", "att
 # counter reads for a 256 MiB device copy (FETCH x2.0, WRITE x1.0); see
 # profiles/attn_fwd_headline_counters.md. Valid only for the kernel sources
 # with this SHA-256; any change to them reports traffic as null.
-TRAFFIC = {"sources_sha256": "dbcbdb465a99a1b9246a6e050fda54f05c06bfbc1bd63c6d85dae49f8876e515",
-           "fetch_kib": 196768.0, "write_kib": 133120.0, "fetch_scale": 2.0, "write_scale": 1.0}
+TRAFFIC = {"sources_sha256": "f50e50ad9d246464e4dc8cb1d9eefc27e7ed10a75e475fec4b60e5a753dec171",
+           "fetch_kib": 196768.2, "write_kib": 133120.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def kernel_sources_sha256() -> str:
