@@ -26,8 +26,8 @@ EXPORTS = ["attn_fwd", "attn_fwd_ex", "attn_fwd_check", "attn_fwd_opts_init", "a
            "attn_fwd_gqa", "attn_fwd_gqa_check", "attn_fwd_varlen", "attn_fwd_varlen_check",
            "attn_bwd", "attn_bwd_check", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size",
            "attn_fwd_fp8", "attn_fwd_fp8_check", "attn_bwd_varlen", "attn_bwd_varlen_check",
-           "attn_fwd_splitkv_noalloc", "attn_fwd_fp8_ex"]
-ABI_VERSION = 9
+           "attn_fwd_splitkv_noalloc", "attn_fwd_fp8_ex", "attn_bwd_ex"]
+ABI_VERSION = 10
 SCHEDULE_PIPELINED, SCHEDULE_REFERENCE = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
 
@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         bwd_args = [vp] * 10 + [i, i, i, i, i, i, f]
         L.attn_bwd.argtypes = bwd_args + [vp]
         L.attn_bwd.restype = i
+        L.attn_bwd_ex.argtypes = bwd_args + [i, vp]
+        L.attn_bwd_ex.restype = i
         L.attn_bwd_check.argtypes = bwd_args
         L.attn_bwd_check.restype = i
         bwdv_args = [vp] * 11 + [i, i, i, i, i, i, i, f]
@@ -308,6 +310,12 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, causal, 
     return lib().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, int(causal), scale, stream)
 
 
+def attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, causal, scale, schedule, stream) -> int:
+    """The C entry point with a kernel schedule; returns the status code."""
+    return lib().attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, int(causal), scale, schedule,
+                             stream)
+
+
 def attn_bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, causal, scale) -> int:
     return lib().attn_bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, int(causal), scale)
 
@@ -315,12 +323,14 @@ def attn_bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, ca
 def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
                        dout: torch.Tensor, causal: bool = False, scale: float | None = None, *,
                        dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
-                       dv: torch.Tensor | None = None, delta: torch.Tensor | None = None):
+                       dv: torch.Tensor | None = None, delta: torch.Tensor | None = None,
+                       schedule: int = SCHEDULE_PIPELINED):
     """Exact attention backward on the current stream: returns (dQ, dK, dV, delta).
 
     q, o, dout: bfloat16 [B,H,N,d]; k, v: bfloat16 [B,Hkv,N,d]; lse: float32 [B,H,N]
     (o and lse from the forward pass with the same causal flag and scale). delta
-    (float32 [B,H,N]) holds D_i = dout_i . o_i.
+    (float32 [B,H,N]) holds D_i = dout_i . o_i. schedule=SCHEDULE_REFERENCE computes
+    dK and dV with the one-wavefront kernel (the race check of attn_bwd_ex).
     """
     _check_tensor("q", q)
     B, H, N, d = q.shape
@@ -343,9 +353,9 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: tor
         _check_tensor(name, t, shape, q.device)
     _check_buffer("delta", delta, torch.float32, (B, H, N), q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, Hkv, N, d, causal, scale,
-                  stream)
+    st = attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, Hkv, N, d, causal, scale,
+                     schedule, stream)
     if st != ATTN_OK:
         raise AttnError(st, last_error())
     return dq, dk, dv, delta

@@ -99,14 +99,20 @@ attn_status_t validate_varlen(const void* q, const void* k, const void* v, const
 // nb: batch (dense) or number of sequences (packed); grids (dense) B*H*n_tiles and
 // B*Hkv*n_tiles, (packed) H*nseq*n_tiles and Hkv*nseq*n_tiles.
 template <int D, bool CAUSAL, bool VARLEN>
-hipError_t launch(const attn_grad::BwdParams& p, int nb, int Hkv, hipStream_t stream) {
+hipError_t launch(const attn_grad::BwdParams& p, int nb, int Hkv, hipStream_t stream, bool reference = false) {
   void* args[] = {const_cast<attn_grad::BwdParams*>(&p)};
   const dim3 block(64 * attn_grad::kWaves);
   // dq first: it stores D, which the dkdv kernel reads (same stream, in order)
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_grad::attn_bwd_dq_kernel<D, CAUSAL, VARLEN>),
                                  dim3(nb * p.H * p.n_tiles), block, args, 0, stream);
   if (e != hipSuccess) return e;
-  // D = 128: wavefront pairs (two wavefronts per key block, eight per workgroup)
+  // D = 128: wavefront pairs (two wavefronts per key block, eight per workgroup); the
+  // reference schedule (dense layout only) runs the one-wavefront kernel instead
+  if constexpr (D == 128 && !VARLEN) {
+    if (reference)
+      return hipLaunchKernel(reinterpret_cast<const void*>(&attn_grad::attn_bwd_dkdv_kernel<D, CAUSAL, false>),
+                             dim3(nb * Hkv * p.n_tiles), block, args, 0, stream);
+  }
   if constexpr (D == 128)
     return hipLaunchKernel(reinterpret_cast<const void*>(&attn_grad::attn_bwd_dkdv_pair_kernel<D, CAUSAL, VARLEN>),
                            dim3(nb * Hkv * p.n_tiles), dim3(2 * 64 * attn_grad::kWaves), args, 0, stream);
@@ -116,9 +122,11 @@ hipError_t launch(const attn_grad::BwdParams& p, int nb, int Hkv, hipStream_t st
 }
 
 template <bool VARLEN>
-hipError_t launch_any(const attn_grad::BwdParams& p, int d, bool causal, int nb, int Hkv, hipStream_t s) {
+hipError_t launch_any(const attn_grad::BwdParams& p, int d, bool causal, int nb, int Hkv, hipStream_t s,
+                      bool reference = false) {
   if (d == 128)
-    return causal ? launch<128, true, VARLEN>(p, nb, Hkv, s) : launch<128, false, VARLEN>(p, nb, Hkv, s);
+    return causal ? launch<128, true, VARLEN>(p, nb, Hkv, s, reference)
+                  : launch<128, false, VARLEN>(p, nb, Hkv, s, reference);
   return causal ? launch<64, true, VARLEN>(p, nb, Hkv, s) : launch<64, false, VARLEN>(p, nb, Hkv, s);
 }
 
@@ -157,18 +165,28 @@ attn_status_t attn_bwd_check(const void* q, const void* k, const void* v, const 
   return validate(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, scale, &work);
 }
 
-attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                       const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int Hkv, int N,
-                       int d, int causal, float scale, void* stream) {
+attn_status_t attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int Hkv, int N,
+                          int d, int causal, float scale, int schedule, void* stream) {
   bool work = false;
-  const attn_status_t st = validate(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, scale, &work);
+  attn_status_t st = validate(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, scale, &work);
+  if (st == ATTN_OK && schedule != ATTN_SCHEDULE_PIPELINED && schedule != ATTN_SCHEDULE_REFERENCE)
+    return fail(ATTN_ERR_OPTS, "unknown schedule %d", schedule);
   if (st != ATTN_OK || !work) return st;
   attn_grad::BwdParams p = make_params(q, k, v, o, lse, dout, dq, dk, dv, delta, H, Hkv, scale);
   p.N = N;
   p.n_tiles = (N + attn_grad::kRows - 1) / attn_grad::kRows;
-  const hipError_t e = launch_any<false>(p, d, causal != 0, B, Hkv, (hipStream_t)stream);
+  const hipError_t e =
+      launch_any<false>(p, d, causal != 0, B, Hkv, (hipStream_t)stream, schedule == ATTN_SCHEDULE_REFERENCE);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ATTN_OK;
+}
+
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int Hkv, int N,
+                       int d, int causal, float scale, void* stream) {
+  return attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, causal, scale,
+                     ATTN_SCHEDULE_PIPELINED, stream);
 }
 
 attn_status_t attn_bwd_varlen_check(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -70,8 +70,10 @@ struct BwdParams {
 
 // Four wavefronts per workgroup (one per SIMD). The dq kernel (and the dk/dv kernel
 // at D = 64) fits two workgroups per compute unit, so each SIMD runs two wavefronts
-// whose matrix and vector work overlap; the dk/dv kernel at D = 128 holds two
-// 128-feature accumulators per lane and runs one (two would spill).
+// whose matrix and vector work overlap. At D = 128 the one-wavefront dk/dv kernel
+// holds two 128-feature accumulators per lane and runs one workgroup per compute
+// unit; it serves as the reference schedule there, and the wavefront-pair kernel
+// below (one accumulator per wavefront, eight wavefronts) does the work.
 constexpr int kWaves = 4;
 constexpr int kRows = 32 * kWaves;   // rows a workgroup owns
 constexpr int kTile = 64;            // rows of the streamed tiles

@@ -56,6 +56,23 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        int Hkv, int N, int d, int causal, float scale, void* stream);
 
 /*
+ * attn_bwd_ex - attn_bwd with a kernel schedule (ABI 10).
+ *   schedule : ATTN_SCHEDULE_PIPELINED (what attn_bwd runs) or
+ *              ATTN_SCHEDULE_REFERENCE, a race check for d = 128: dK and dV come
+ *              from the one-wavefront dk/dv kernel, which keeps both accumulators
+ *              and P in one lane, instead of the wavefront pairs that pass P
+ *              through LDS between two wavefronts. Both accumulate every product
+ *              in the same order, so dk and dv must be equal bit for bit; dq and
+ *              delta come from the same kernel either way. At d = 64 both
+ *              schedules run the one-wavefront kernel.
+ * Same arguments and error codes as attn_bwd; ATTN_ERR_OPTS for another schedule
+ * value.
+ */
+attn_status_t attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
+                          int Hkv, int N, int d, int causal, float scale, int schedule, void* stream);
+
+/*
  * attn_bwd_varlen - backward of packed variable-length attention (the layout of
  * attn_fwd_varlen in attn_fwd.h: several sequences folded into the token axis).
  *   q, o, dout, dq : bf16 [H][total][d]; k, v, dk, dv : bf16 [Hkv][total][d];

@@ -51,8 +51,9 @@ extern "C" {
  * 6: adds attn_fwd_fp8 and attn_fwd_fp8_check (FP8 e4m3 inputs, declared in attn_fp8.h).
  * 7: adds attn_bwd_varlen and attn_bwd_varlen_check (declared in attn_bwd.h).
  * 8: adds attn_fwd_splitkv_noalloc.
- * 9: adds the schedule option (attn_fwd_opts.schedule) and attn_fwd_fp8_ex. */
-#define ATTN_ABI_VERSION 9
+ * 9: adds the schedule option (attn_fwd_opts.schedule) and attn_fwd_fp8_ex.
+ * 10: adds attn_bwd_ex (the backward pass with a schedule, declared in attn_bwd.h). */
+#define ATTN_ABI_VERSION 10
 
 typedef enum attn_status {
   ATTN_OK = 0,

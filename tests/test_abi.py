@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == set(bnd.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.attn_abi_version() == bnd.ABI_VERSION == 9
+    assert lib.attn_abi_version() == bnd.ABI_VERSION == 10
 
 
 def check(*args, **kw):
@@ -261,6 +261,22 @@ def test_bwd_valid_and_empty():
     assert bwd_check(Q, K, V, O, L, DO, DQ, DK, DV, DL, 2, 32, 8, 8192, 128, 1, 0.088) == bnd.ATTN_OK
     assert bwd_check(*([None] * 10), 0, 4, 2, 16, 64, 0, 1.0) == bnd.ATTN_OK
     assert bnd.attn_bwd(*([None] * 10), 1, 4, 2, 0, 64, 0, 1.0, None) == bnd.ATTN_OK
+
+
+def test_bwd_ex_schedule_checked_before_any_launch():
+    # an unknown schedule is rejected after the argument checks, before any launch
+    # (the pointers are host-side stand-ins; nothing is launched)
+    args = [Q, K, V, O, L, DO, DQ, DK, DV, DL, 1, 4, 2, 64, 128, 0, 1.0]
+    assert bnd.attn_bwd_ex(*args, 7, None) == 8  # ATTN_ERR_OPTS
+    assert "schedule" in bnd.last_error()
+    assert bnd.attn_bwd_ex(*args, -1, None) == 8
+    # argument errors come first, and an empty problem launches nothing with either schedule
+    bad = list(args)
+    bad[14] = 96
+    assert bnd.attn_bwd_ex(*bad, 1, None) == 3
+    empty = [None] * 10 + [1, 4, 2, 0, 128, 0, 1.0]
+    for sched in (bnd.SCHEDULE_PIPELINED, bnd.SCHEDULE_REFERENCE):
+        assert bnd.attn_bwd_ex(*empty, sched, None) == bnd.ATTN_OK
 
 
 @pytest.mark.parametrize("patch,code", [

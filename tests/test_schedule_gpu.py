@@ -16,7 +16,8 @@ query tiles than compute units, so each workgroup issues the next tile's loads
 during this tile's epilogue), ragged key tails, causal diagonals, grouped-query
 heads, packed variable-length sequences (including sequences shorter than one key
 tile) and split keys; the drifting inputs and tau = 0 make rows rescale often, so
-the rescale branch runs between loads. The FP8 kernel is checked the same way.
+the rescale branch runs between loads. The FP8 kernel is checked the same way, and
+the backward's wavefront-pair dk/dv kernel against the one-wavefront kernel.
 """
 import math
 
@@ -132,6 +133,37 @@ def test_fp8_schedules_agree_bitwise(B, H, N, d, causal, drift, tau):
     same_bits(l1, l2, "LSE")
 
 
+# Backward at d = 128: the dk/dv kernel runs in wavefront pairs that pass P through
+# LDS (one wavefront forms S, P and dV, the other dP, dS and dK, with the tile loads
+# issued by the second); the reference schedule computes dK and dV with the
+# one-wavefront kernel, which keeps P in its lanes and accumulates every product in
+# the same order. A missing or misplaced wait around the P buffer, the LSE tile or
+# the tile loads would change some element of dK or dV. (d = 64 runs the
+# one-wavefront kernel either way; one shape checks that the option is accepted.)
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", [
+    (2, 8, 8, 1024, 128, False),   # several query tiles per key block, full tiles
+    (1, 8, 2, 1000, 128, True),    # grouped-query heads (4 per K/V head), causal, ragged
+    (1, 4, 1, 777, 128, True),     # multi-query, causal, ragged
+    (1, 4, 4, 37, 128, False),     # shorter than one tile
+    (2, 4, 4, 513, 64, True),      # d = 64
+])
+def test_backward_schedules_agree_bitwise(B, H, Hkv, N, d, causal):
+    note(f"schedules backward: B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal}")
+    q, k, v = inputs.draw_gqa(B, H, Hkv, N, d, seed=36000 + N + d + H)
+    do = inputs.draw(B, H, N, d, seed=36500 + N)[0]
+    dev = device()
+    q, k, v, do = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = binding.attention(q, k, v, causal=causal, scale=scale)
+    g1 = binding.attention_backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+    g2 = binding.attention_backward(q, k, v, o, lse, do, causal=causal, scale=scale, schedule=REF)
+    torch.cuda.synchronize()
+    for x in g1:
+        assert torch.isfinite(x.float()).all()
+    for name, a, b in zip(("dQ", "dK", "dV", "delta"), g1, g2):
+        same_bits(a, b, name)
+
+
 def test_reference_schedule_rejects_what_it_does_not_cover():
     dev = device()
     q, k, v = (t.to(dev) for t in inputs.draw(1, 1, 64, 64, seed=35000))
@@ -141,3 +173,6 @@ def test_reference_schedule_rejects_what_it_does_not_cover():
         binding.attention(q, k, v, scale=-0.125, schedule=REF)
     with pytest.raises(binding.AttnError, match="ATTN_ERR_OPTS"):
         binding.attention(q, k, v, schedule=2)
+    o, lse = binding.attention(q, k, v)
+    with pytest.raises(binding.AttnError, match="ATTN_ERR_OPTS"):
+        binding.attention_backward(q, k, v, o, lse, q, schedule=2)
