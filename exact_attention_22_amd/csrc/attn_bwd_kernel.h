@@ -344,16 +344,25 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) 
       for (int j = 0; j < RT; ++j) trd(j);
       // dS^T in the B-operand order of the next product: k-step 2*cc + hh holds keys
       // 32*cc + 16*hh + 8*(j/4) + 4*hl + j%4 (register r = 8*hh + j of the block).
+      // The masked form runs only on boundary tiles (a branch on the wavefront-uniform
+      // `edge`): written as one loop with a select, the compiler if-converts the mask
+      // and every tile pays its compares and selects.
       bf16x8 dsb[2];
+      auto ds_block = [&](auto masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -lse2));
-        if (edge) {
-          const int key = j0 + 32 * cc + 8 * (r / 4) + 4 * hl + (r % 4);
-          pr = (key >= N || (CAUSAL && key > my_q)) ? 0.f : pr;
+        for (int r = 0; r < 16; ++r) {
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -lse2));
+          if (decltype(masked)::value) {
+            const int key = j0 + 32 * cc + 8 * (r / 4) + 4 * hl + (r % 4);
+            pr = (key >= N || (CAUSAL && key > my_q)) ? 0.f : pr;
+          }
+          dsb[r / 8][r % 8] = (__bf16)(pr * (dp[r] - Di));
         }
-        dsb[r / 8][r % 8] = (__bf16)(pr * (dp[r] - Di));
-      }
+      };
+      if (edge)
+        ds_block(std::true_type{});
+      else
+        ds_block(std::false_type{});
 #pragma unroll
       for (int j = 0; j < NTR; ++j) {
         if (j + RT < NTR) trd(j + RT);
@@ -463,6 +472,15 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(co
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dO, 32 * cc + l32, 2 * kk + hl), vreg[kk], dp, 0, 0,
                                                      0);
       }
+      // Boundary tiles hide their scores first (as -inf, so P = 2^-inf = 0) in a branch
+      // of their own; the rest of the block is the same code for every tile.
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = iq0 + 32 * cc + 8 * (r / 4) + 4 * hl + (r % 4);
+          s[r] = (qi >= N || (CAUSAL && my_k > qi)) ? -INFINITY : s[r];
+        }
+      }
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
@@ -472,11 +490,7 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(co
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * gq + e;
-          float pr = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -l4[e] * 1.44269504088896341f));
-          if (edge) {
-            const int qi = iq0 + qr + e;
-            pr = (qi >= N || (CAUSAL && my_k > qi)) ? 0.f : pr;
-          }
+          const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -l4[e] * 1.44269504088896341f));
           pb[r / 8][r % 8] = (__bf16)pr;
           dsb[r / 8][r % 8] = (__bf16)(pr * (dp[r] - d4[e]));
         }
