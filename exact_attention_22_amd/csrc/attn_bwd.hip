@@ -150,6 +150,7 @@ attn_grad::BwdParams make_params(const void* q, const void* k, const void* v, co
   p.G = H / Hkv;
   p.scale = scale;
   p.c = scale * 1.44269504088896341f;
+  p.n_xcd = attn_host::device_shape().xcds;
   return p;
 }
 

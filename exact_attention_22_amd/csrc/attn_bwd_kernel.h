@@ -66,7 +66,23 @@ struct BwdParams {
   int n_tiles;        // ceil(N / 128) row tiles per head (packed: per longest sequence)
   float scale;
   float c;            // scale * log2(e)
+  int n_xcd;          // XCDs the dispatcher deals workgroups to in turn (1: no renumbering)
 };
+
+// Workgroup number in XCD-major order. The dispatcher deals workgroups to the n_xcd
+// XCDs in turn (workgroup i to XCD i mod n_xcd); renumbered, each XCD holds a
+// contiguous range of (head, row tile), so the workgroups of one head, which load
+// the same tiles at about the same time, share one L2. The identity when the grid
+// does not divide evenly.
+__device__ __forceinline__ int xcd_major_block(int n_xcd) {
+#ifdef ATTN_X_NOXCD
+  return blockIdx.x;
+#else
+  const int n = gridDim.x, b = blockIdx.x;
+  if (n_xcd <= 1 || n % n_xcd) return b;
+  return (b % n_xcd) * (n / n_xcd) + b / n_xcd;
+#endif
+}
 
 // Four wavefronts per workgroup (one per SIMD). The dq kernel (and the dk/dv kernel
 // at D = 64) fits two workgroups per compute unit, so each SIMD runs two wavefronts
@@ -253,8 +269,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
-  const int hb = blockIdx.x / p.n_tiles;
-  const int i0 = (blockIdx.x - hb * p.n_tiles) * kRows;
+  const int blk = xcd_major_block(p.n_xcd);
+  const int hb = blk / p.n_tiles;
+  const int i0 = (blk - hb * p.n_tiles) * kRows;
   int N;             // rows (and keys) of this workgroup's sequence
   size_t qrow0, kvrow0;  // first row of the query head / key-value head in memory
   if (VARLEN) {
@@ -402,8 +419,9 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(co
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
   const int Hkv = p.H / p.G;
-  const int bg = blockIdx.x / p.n_tiles;  // dense: b * Hkv + g; packed: g * nseq + sequence
-  const int j0w = (blockIdx.x - bg * p.n_tiles) * kRows;
+  const int blk = xcd_major_block(p.n_xcd);
+  const int bg = blk / p.n_tiles;  // dense: b * Hkv + g; packed: g * nseq + sequence
+  const int j0w = (blk - bg * p.n_tiles) * kRows;
   int N, g;
   size_t kvrow0, qrow_first, qrow_step;  // query head hq starts at row qrow_first + hq * qrow_step
   if (VARLEN) {
@@ -559,8 +577,9 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(const BwdPar
   const bool pw = wv < kWaves;  // P wavefront (K, dV) or dS wavefront (V, dK)
   const int l32 = lane & 31, hl = lane >> 5;
   const int Hkv = p.H / p.G;
-  const int bg = blockIdx.x / p.n_tiles;  // dense: b * Hkv + g; packed: g * nseq + sequence
-  const int j0w = (blockIdx.x - bg * p.n_tiles) * kRows;
+  const int blk = xcd_major_block(p.n_xcd);
+  const int bg = blk / p.n_tiles;  // dense: b * Hkv + g; packed: g * nseq + sequence
+  const int j0w = (blk - bg * p.n_tiles) * kRows;
   int N, g;
   size_t kvrow0, qrow_first, qrow_step;  // query head hq starts at row qrow_first + hq * qrow_step
   if (VARLEN) {
