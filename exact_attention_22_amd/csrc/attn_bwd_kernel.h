@@ -271,7 +271,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) 
   const int l32 = lane & 31, hl = lane >> 5;
   const int blk = xcd_major_block(p.n_xcd);
   const int hb = blk / p.n_tiles;
-  const int i0 = (blk - hb * p.n_tiles) * kRows;
+  const int tile = blk - hb * p.n_tiles;
+  // causal: a query block sees the key tiles up to its own, so the longest blocks
+  // start first and the short ones fill in at the end
+  const int i0 = (CAUSAL ? p.n_tiles - 1 - tile : tile) * kRows;
   int N;             // rows (and keys) of this workgroup's sequence
   size_t qrow0, kvrow0;  // first row of the query head / key-value head in memory
   if (VARLEN) {
