@@ -150,7 +150,9 @@ attn_grad::BwdParams make_params(const void* q, const void* k, const void* v, co
   p.G = H / Hkv;
   p.scale = scale;
   p.c = scale * 1.44269504088896341f;
-  p.n_xcd = attn_host::device_shape().xcds;
+  const attn_host::DeviceShape ds = attn_host::device_shape();
+  p.n_xcd = ds.xcds;
+  p.cus_per_xcd = ds.cus / ds.xcds;
   return p;
 }
 

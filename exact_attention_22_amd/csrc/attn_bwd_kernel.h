@@ -67,21 +67,37 @@ struct BwdParams {
   float scale;
   float c;            // scale * log2(e)
   int n_xcd;          // XCDs the dispatcher deals workgroups to in turn (1: no renumbering)
+  int cus_per_xcd;    // compute units of one XCD
 };
 
-// Workgroup number in XCD-major order. The dispatcher deals workgroups to the n_xcd
-// XCDs in turn (workgroup i to XCD i mod n_xcd); renumbered, each XCD holds a
-// contiguous range of (head, row tile), so the workgroups of one head, which load
-// the same tiles at about the same time, share one L2. The identity when the grid
+// (head, row tile) of this workgroup: bg = head index (dense b * heads + h; packed
+// h * nseq + sequence), rank = row tile in the kernel's own order (rank 0 is the
+// tile with the most work under causal masking).
+// The dispatcher deals workgroups to the n_xcd XCDs in turn (workgroup i to XCD
+// i mod n_xcd); numbered XCD-major, each XCD holds a contiguous range of whole heads,
+// so the workgroups of one head, which load the same tiles at about the same time,
+// share one L2. Under causal masking the row tiles differ in length; when a head has
+// no more tiles than the XCD runs workgroups at once (PER_CU per compute unit), the
+// XCD runs several heads together anyway, and within its range the workgroups go by
+// rank first, so every head's long tiles start before any short one (with more tiles
+// per head, head order keeps one head's workgroups together and the short tiles of
+// one head fill in beside the long ones of the next). Plain numbering when the grid
 // does not divide evenly.
-__device__ __forceinline__ int xcd_major_block(int n_xcd) {
-#ifdef ATTN_X_NOXCD
-  return blockIdx.x;
-#else
-  const int n = gridDim.x, b = blockIdx.x;
-  if (n_xcd <= 1 || n % n_xcd) return b;
-  return (b % n_xcd) * (n / n_xcd) + b / n_xcd;
-#endif
+struct BlockCoords {
+  int bg, rank;
+};
+template <bool CAUSAL, int PER_CU>
+__device__ __forceinline__ BlockCoords block_coords(const BwdParams& p) {
+  const int n = gridDim.x, b = blockIdx.x, n_xcd = p.n_xcd, n_tiles = p.n_tiles;
+  const bool split = n_xcd > 1 && n % n_xcd == 0;
+  const int per = split ? n / n_xcd : n;  // workgroups of one XCD
+  const int blk = split ? (b % n_xcd) * per + b / n_xcd : b;
+  if (CAUSAL && per % n_tiles == 0 && n_tiles <= PER_CU * p.cus_per_xcd) {
+    const int heads = per / n_tiles;  // whole heads per XCD range
+    const int base = blk - blk % per, k = blk - base;
+    return {base / n_tiles + k % heads, k / heads};
+  }
+  return {blk / n_tiles, blk % n_tiles};
 }
 
 // Four wavefronts per workgroup (one per SIMD). The dq kernel (and the dk/dv kernel
@@ -269,12 +285,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
-  const int blk = xcd_major_block(p.n_xcd);
-  const int hb = blk / p.n_tiles;
-  const int tile = blk - hb * p.n_tiles;
-  // causal: a query block sees the key tiles up to its own, so the longest blocks
-  // start first and the short ones fill in at the end
-  const int i0 = (CAUSAL ? p.n_tiles - 1 - tile : tile) * kRows;
+  const BlockCoords bc = block_coords<CAUSAL, 2>(p);
+  const int hb = bc.bg;
+  // causal: a query block sees the key tiles up to its own, so rank 0 is the last block
+  const int i0 = (CAUSAL ? p.n_tiles - 1 - bc.rank : bc.rank) * kRows;
   int N;             // rows (and keys) of this workgroup's sequence
   size_t qrow0, kvrow0;  // first row of the query head / key-value head in memory
   if (VARLEN) {
@@ -422,9 +436,10 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) attn_bwd_dkdv_kernel(co
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
   const int Hkv = p.H / p.G;
-  const int blk = xcd_major_block(p.n_xcd);
-  const int bg = blk / p.n_tiles;  // dense: b * Hkv + g; packed: g * nseq + sequence
-  const int j0w = (blk - bg * p.n_tiles) * kRows;
+  // causal: a key block sees the query tiles from its own on, so rank 0 is block 0
+  const BlockCoords bc = block_coords<CAUSAL, D == 128 ? 1 : 2>(p);
+  const int bg = bc.bg;  // dense: b * Hkv + g; packed: g * nseq + sequence
+  const int j0w = bc.rank * kRows;
   int N, g;
   size_t kvrow0, qrow_first, qrow_step;  // query head hq starts at row qrow_first + hq * qrow_step
   if (VARLEN) {
@@ -580,9 +595,10 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(const BwdPar
   const bool pw = wv < kWaves;  // P wavefront (K, dV) or dS wavefront (V, dK)
   const int l32 = lane & 31, hl = lane >> 5;
   const int Hkv = p.H / p.G;
-  const int blk = xcd_major_block(p.n_xcd);
-  const int bg = blk / p.n_tiles;  // dense: b * Hkv + g; packed: g * nseq + sequence
-  const int j0w = (blk - bg * p.n_tiles) * kRows;
+  // causal: a key block sees the query tiles from its own on, so rank 0 is block 0
+  const BlockCoords bc = block_coords<CAUSAL, 1>(p);
+  const int bg = bc.bg;  // dense: b * Hkv + g; packed: g * nseq + sequence
+  const int j0w = bc.rank * kRows;
   int N, g;
   size_t kvrow0, qrow_first, qrow_step;  // query head hq starts at row qrow_first + hq * qrow_step
   if (VARLEN) {
