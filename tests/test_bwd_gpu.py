@@ -54,6 +54,11 @@ def draw(B, H, Hkv, N, d, seed):
     (1, 3, 3, 33, 128, True),
     (2, 2, 1, 200, 64, False),
     (1, 2, 2, 640, 128, False),
+    # causal grids that divide evenly over 8 XCDs with few row tiles per head: both
+    # kernels take the rank-major workgroup order (longest tiles of several heads first)
+    (2, 8, 8, 512, 128, True),
+    (4, 8, 4, 1024, 128, True),
+    (2, 8, 4, 512, 64, True),
 ])
 def test_backward_full(B, H, Hkv, N, d, causal):
     note(f"backward full: B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal}")
