@@ -224,6 +224,12 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Keeps the matrix products and LDS reads on either side in source order (vector
+// and scalar ALU work may still move across): operand reads written a few products
+// ahead then stay ahead, where the scheduler would otherwise sink each read to just
+// before its product and make the product wait for it.
+__device__ __forceinline__ void keep_order() { __builtin_amdgcn_sched_barrier(0x0002 | 0x0004 | 0x0400); }
+
 // Per-lane byte offsets of the A operands in a swizzled [64][D] LDS tile,
 // independent of the buffer and of the 32-row block (row reads) or 16-row group
 // (transpose reads): those add a constant that the read instruction carries.
@@ -364,12 +370,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) 
         if (f + RA < NRF) rd(f + RA);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[f], qreg[kk], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[f], doreg[kk], dp, 0, 0, 0);
-      }
-      if (cc == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * RA, 0);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (cc * KK + kk + RA < NRF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        keep_order();
       }
       // transpose operands of this block's dQ products, i = 2 * hh + ... (hh, mt)
       bf16x8 tq[NTR];
@@ -401,6 +402,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const BwdParams p) 
       for (int j = 0; j < NTR; ++j) {
         if (j + RT < NTR) trd(j + RT);
         acc[j % MT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[j], dsb[j / MT], acc[j % MT], 0, 0, 0);
+        keep_order();
       }
     }
     sync_tiles();
