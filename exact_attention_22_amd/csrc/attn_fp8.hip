@@ -93,8 +93,10 @@ attn_status_t attn_fwd_fp8_ex(const void* q, const void* k, const void* vt, void
   const int rows = d == 128 ? attn_fp8::Shape<128>::ROWS : attn_fp8::Shape<64>::ROWS;
   p.nq_tiles = (N + rows - 1) / rows;
   p.total_tiles = B * H * p.nq_tiles;
-  p.n_xcd = attn_host::device_shape().xcds;
+  const attn_host::DeviceShape ds = attn_host::device_shape();
+  p.n_xcd = ds.xcds;
   p.per_xcd = (p.total_tiles + p.n_xcd - 1) / p.n_xcd;
+  p.cus_per_xcd = ds.cus / ds.xcds;
   p.c = scale * q_scale * k_scale * 1.44269504088896341f;
   p.ov = v_scale;
   p.tau = tau;

@@ -105,6 +105,7 @@ struct Fp8Params {
   int total_tiles;    // B * H * nq_tiles
   int n_xcd;          // XCDs of the device (workgroup slot i runs on XCD i % n_xcd)
   int per_xcd;        // ceil(total_tiles / n_xcd)
+  int cus_per_xcd;    // compute units of one XCD
   float c;            // scale * q_scale * k_scale * log2(e) (> 0)
   float ov;           // v_scale
   float tau;          // rescale threshold, log2 units, in [0, 8]
@@ -239,12 +240,25 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, Shape<D>::PER_CU) attn_fwd_
   // XCD-aware tile order: workgroups are dealt round-robin to the X XCDs, so slot
   // i runs tile (i % X) * per_xcd + i / X and each XCD works through a contiguous
   // range (the query tiles of a head share that XCD's L2 for their K/V reads).
+  // Causal: longest query tiles first. When the range holds whole heads of no more
+  // tiles than the XCD runs workgroups at once, it runs several heads together
+  // anyway, and the range goes by tile rank first (every head's long tiles before
+  // any short one); otherwise head by head, longest first within each.
   const int slot = blockIdx.x;
-  const int tile = (slot % p.n_xcd) * p.per_xcd + slot / p.n_xcd;
-  if (tile >= p.total_tiles) return;
-  const int bh = tile / p.nq_tiles;
-  int qt = tile % p.nq_tiles;
-  if (CAUSAL) qt = p.nq_tiles - 1 - qt;  // longest query tiles first
+  const int x = slot % p.n_xcd, k = slot / p.n_xcd;  // XCD, position in its range
+  int bh, qt;
+  if (CAUSAL && p.per_xcd % p.nq_tiles == 0 && p.nq_tiles <= Shape<D>::PER_CU * p.cus_per_xcd) {
+    const int heads = p.per_xcd / p.nq_tiles;
+    bh = x * heads + k % heads;
+    if (bh * p.nq_tiles >= p.total_tiles) return;
+    qt = p.nq_tiles - 1 - k / heads;
+  } else {
+    const int tile = x * p.per_xcd + k;
+    if (tile >= p.total_tiles) return;
+    bh = tile / p.nq_tiles;
+    qt = tile % p.nq_tiles;
+    if (CAUSAL) qt = p.nq_tiles - 1 - qt;
+  }
 
   const int tid = threadIdx.x;
   // wave index in a scalar register: the tile loads' LDS destinations are then scalar
