@@ -46,6 +46,10 @@ def check_rows(o, lse, o_ref, lse_ref, bo, bl, what):
     (1, 1, 17, 64, True),
     (1, 2, 1000, 128, True),
     (2, 1, 640, 64, False),
+    # causal grids whose XCD ranges hold several whole heads of few query tiles: the
+    # workgroups go by tile rank first (longest tiles of every head first)
+    (2, 8, 512, 128, True),
+    (4, 4, 512, 64, True),
 ])
 def test_fp8_full(B, H, N, d, causal):
     note(f"fp8: B={B} H={H} N={N} d={d} causal={causal}")
