@@ -318,6 +318,9 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, Shape<D>::PER_CU) attn_fwd_
 
     // S^T = K Q^T for the two 32-row blocks of the K tile
     f32x16 s[2];
+    // Issue priority up while this wavefront feeds the matrix core, so the other
+    // wavefronts' softmax work on the same SIMD does not delay its products.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       s[cc] = f32x16{};
@@ -325,6 +328,7 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, Shape<D>::PER_CU) attn_fwd_
 #pragma unroll
       for (int m = 0; m < MQ; ++m) s[cc] = mma(read32<D>(kb, r, 4 * m + 2 * hl, kswz<D>(r)), qreg[m], s[cc]);
     }
+    __builtin_amdgcn_s_setprio(0);
 
     // register r of block cc holds key j0 + 32 hl + 16 cc + r; mask keys past N and
     // (causal) keys after the query, on boundary tiles only
@@ -402,8 +406,10 @@ __global__ void __launch_bounds__(64 * Shape<D>::NW, Shape<D>::PER_CU) attn_fwd_
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) va[mt] = mask_tail(va[mt], hl, N - j0);
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) oacc[mt] = mma(va[mt], pb, oacc[mt]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   if (REF) {
